@@ -1,0 +1,305 @@
+// qmv_api.hip -- the C ABI of include/qmv.h: argument validation, launch
+// planning and dispatch to the gfx950 kernel instances.
+//
+// Validation is plain host code and runs before any HIP call, so every error
+// path is reachable (and tested) on a machine without a GPU.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstddef>
+#include <cstdint>
+#include <mutex>
+
+#include "qmv.h"
+#include "qmv_dispatch.hpp"
+
+namespace {
+
+using qmv::KernelFn;
+using qmv::Params;
+
+constexpr int kWavesPerWg = 8;
+
+int dtype_bytes(int dt) { return dt == QMV_DT_F32 ? 4 : 2; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb)
+{
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return a0 < b0 + nb && b0 < a0 + na;
+}
+
+int r_index(int R) { return R == 1 ? 0 : (R == 2 ? 1 : 2); }
+
+// Pure argument check (no HIP calls).
+int check_args(const uint32_t* w, const void* s, const void* b, const void* x, void* y, int M,
+               int N, int K, int bits, int gs, int x_dt, int sb_dt, int y_dt, int R)
+{
+    if (!w || !s || !b || !x || !y) return QMV_E_NULL;
+    if (bits != 2 && bits != 4) return QMV_E_BITS;
+    if (gs != 64 && gs != 128) return QMV_E_GROUP;
+    if (M < 1 || M > QMV_MAX_M) return QMV_E_M_RANGE;
+    if (N < 1 || N > QMV_MAX_N || K < gs || K > QMV_MAX_K || K % gs != 0) return QMV_E_SHAPE;
+    if (x_dt != QMV_DT_F32 && x_dt != QMV_DT_BF16) return QMV_E_DTYPE;
+    if (sb_dt != QMV_DT_F16 && sb_dt != QMV_DT_BF16) return QMV_E_DTYPE;
+    if (y_dt != QMV_DT_F32 && y_dt != QMV_DT_BF16) return QMV_E_DTYPE;
+    if (R != 0 && R != 1 && R != 2 && R != 4) return QMV_E_ROWS;
+    const long long G = K / gs;
+    if (!aligned(w, 16) || !aligned(s, 16) || !aligned(b, 16) || !aligned(x, 16)) return QMV_E_ALIGN;
+    if (!aligned(y, (size_t)dtype_bytes(y_dt))) return QMV_E_ALIGN;
+    const size_t nw = (size_t)N * (size_t)K * bits / 8;
+    const size_t nsb = (size_t)N * (size_t)G * 2;
+    const size_t nx = (size_t)M * (size_t)K * dtype_bytes(x_dt);
+    const size_t ny = (size_t)M * (size_t)N * dtype_bytes(y_dt);
+    if (overlap(y, ny, w, nw) || overlap(y, ny, s, nsb) || overlap(y, ny, b, nsb) ||
+        overlap(y, ny, x, nx))
+        return QMV_E_ALIAS;
+    return QMV_OK;
+}
+
+KernelFn pick_kernel(int bits, int gs, bool xf32, int R, int M)
+{
+    const int ri = r_index(R);
+    const int mi = M - 1;
+    if (bits == 4 && gs == 64) return xf32 ? qmv::qmv_table_b4_g64_f32[ri][mi] : qmv::qmv_table_b4_g64_bf16[ri][mi];
+    if (bits == 4 && gs == 128) return xf32 ? qmv::qmv_table_b4_g128_f32[ri][mi] : qmv::qmv_table_b4_g128_bf16[ri][mi];
+    if (bits == 2 && gs == 64) return xf32 ? qmv::qmv_table_b2_g64_f32[ri][mi] : qmv::qmv_table_b2_g64_bf16[ri][mi];
+    return xf32 ? qmv::qmv_table_b2_g128_f32[ri][mi] : qmv::qmv_table_b2_g128_bf16[ri][mi];
+}
+
+// Library choice of rows per wavefront.
+int default_rows(int M, int G, bool xf32)
+{
+    (void)G;
+    int R = (M <= 2) ? 2 : 4;
+    if (xf32 && M > 4) R = 2;
+    return R;
+}
+
+struct Plan {
+    Params p;
+    KernelFn fn;
+    int R, W, lds, grid_cap_rb;
+};
+
+// LDS layout and K windows.  Returns QMV_E_SHAPE if one wave step of
+// activations for all M vectors does not fit in LDS.
+int make_plan(int M, int N, int K, int bits, int gs, bool xf32, int R, Plan& pl)
+{
+    const int G = K / gs;
+    const int lpg = gs * bits / 128;
+    const int chunks = K * bits / 128;
+    const int nsteps = (chunks + qmv::kWave - 1) / qmv::kWave;
+    const int W = kWavesPerWg;
+    const int xcb = (128 / bits) * (xf32 ? 4 : 2);
+    int ws = nsteps, x_m = 0, s_bytes = 0, total = 0;
+    for (;;) {
+        const int logical = ws * qmv::kWave * xcb;
+        x_m = logical + logical / 16;
+        s_bytes = M * (ws * qmv::kWave / lpg) * 4;
+        total = M * x_m + s_bytes;
+        if (total <= qmv::kLdsBytes || ws == 1) break;
+        --ws;
+    }
+    if (total > qmv::kLdsBytes) return QMV_E_SHAPE;
+    const int nwin = (nsteps + ws - 1) / ws;
+    ws = (nsteps + nwin - 1) / nwin;  // even windows
+    {
+        const int logical = ws * qmv::kWave * xcb;
+        x_m = logical + logical / 16;
+        s_bytes = M * (ws * qmv::kWave / lpg) * 4;
+    }
+    Params& p = pl.p;
+    p.N = N;
+    p.K = K;
+    p.G = G;
+    p.chunks = chunks;
+    p.nsteps = nsteps;
+    p.win_steps = ws;
+    p.nwin = nwin;
+    p.n_rb = (N + W * R - 1) / (W * R);
+    p.x_m_bytes = x_m;
+    p.gw = ws * qmv::kWave / lpg;
+    p.s_off = M * x_m;
+    pl.lds = p.s_off + ((s_bytes + 15) / 16) * 16;
+    pl.R = R;
+    pl.W = W;
+    pl.fn = pick_kernel(bits, gs, xf32, R, M);
+    return QMV_OK;
+}
+
+// Per-device launch-shape cache: compute-unit count, and for each kernel
+// instance and LDS size the resident workgroups per CU (after raising the
+// instance's dynamic-LDS limit).  Filled on first use; never invalidated.
+struct OccEntry {
+    const void* fn;
+    int dev;
+    int lds;
+    int blocks;
+};
+
+std::mutex g_mu;
+int g_cus[64] = {0};
+OccEntry g_occ[1024];
+int g_nocc = 0;
+
+int cu_count_locked(int dev)
+{
+    if (dev < 0 || dev >= 64) return 256;
+    if (g_cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        g_cus[dev] = n;
+    }
+    return g_cus[dev];
+}
+
+// Workgroups: as many as stay resident (occupancy x CUs), at most one per row
+// block, balanced so every workgroup walks the same number of row blocks.
+// Returns -1 on a HIP error.
+int plan_grid(Plan& pl, int* blocks_per_cu)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return -1;
+    const void* fn = reinterpret_cast<const void*>(pl.fn);
+    std::lock_guard<std::mutex> lk(g_mu);
+    int nb = -1;
+    for (int i = 0; i < g_nocc; ++i)
+        if (g_occ[i].fn == fn && g_occ[i].dev == dev && g_occ[i].lds == pl.lds) {
+            nb = g_occ[i].blocks;
+            break;
+        }
+    if (nb < 0) {
+        if (pl.lds > 65536 &&
+            hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, pl.lds) != hipSuccess)
+            return -1;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, pl.W * qmv::kWave, pl.lds) != hipSuccess)
+            return -1;
+        if (nb < 1) nb = 1;
+        if (g_nocc < 1024) g_occ[g_nocc++] = OccEntry{fn, dev, pl.lds, nb};
+    }
+    if (blocks_per_cu) *blocks_per_cu = nb;
+    const int cap = nb * cu_count_locked(dev);
+    const int n_rb = pl.p.n_rb;
+    const int per = (n_rb + cap - 1) / cap;
+    return (n_rb + per - 1) / per;
+}
+
+// Vectors per launch: all M, unless one wave step of activations for M
+// vectors does not fit in LDS (fp32 activations with 2-bit codes); then the
+// largest count that fits.  Vectors are independent, so splitting M changes
+// no result bit.
+int vectors_per_launch(int M, int N, int K, int bits, int gs, bool xf32, int R_req)
+{
+    for (int mc = M; mc >= 1; --mc) {
+        Plan pl;
+        const int R = R_req ? R_req : default_rows(mc, K / gs, xf32);
+        if (make_plan(mc, N, K, bits, gs, xf32, R, pl) == QMV_OK) return mc;
+    }
+    return 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+int qmv_affine_ex(const uint32_t* w_packed, const void* scales, const void* biases,
+                  const void* x, void* y, int M, int N, int K, int bits, int group_size,
+                  qmv_dtype x_dt, qmv_dtype sb_dt, qmv_dtype y_dt, int rows_per_wave,
+                  void* stream)
+{
+    int st = check_args(w_packed, scales, biases, x, y, M, N, K, bits, group_size, x_dt, sb_dt,
+                        y_dt, rows_per_wave);
+    if (st != QMV_OK) return st;
+    const bool xf32 = (x_dt == QMV_DT_F32);
+    const int G = K / group_size;
+    const int mc = vectors_per_launch(M, N, K, bits, group_size, xf32, rows_per_wave);
+    if (mc < 1) return QMV_E_SHAPE;
+    for (int m0 = 0; m0 < M; m0 += mc) {
+        const int mm = std::min(mc, M - m0);
+        const int R = rows_per_wave ? rows_per_wave : default_rows(mm, G, xf32);
+        Plan pl;
+        st = make_plan(mm, N, K, bits, group_size, xf32, R, pl);
+        if (st != QMV_OK) return st;
+        Params& p = pl.p;
+        p.w = w_packed;
+        p.s = static_cast<const uint16_t*>(scales);
+        p.b = static_cast<const uint16_t*>(biases);
+        p.x = static_cast<const uint8_t*>(x) + (size_t)m0 * K * dtype_bytes(x_dt);
+        p.y = static_cast<uint8_t*>(y) + (size_t)m0 * N * dtype_bytes(y_dt);
+        p.sb_bf16 = (sb_dt == QMV_DT_BF16);
+        p.y_bf16 = (y_dt == QMV_DT_BF16);
+        const int grid = plan_grid(pl, nullptr);
+        if (grid < 1) return QMV_E_LAUNCH;
+        void* args[] = {&p};
+        const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(pl.fn), dim3(grid),
+                                             dim3(pl.W * qmv::kWave), args, (size_t)pl.lds,
+                                             static_cast<hipStream_t>(stream));
+        if (e != hipSuccess) return QMV_E_LAUNCH;
+    }
+    return QMV_OK;
+}
+
+int qmv_affine(const uint32_t* w_packed, const void* scales, const void* biases, const void* x,
+               void* y, int M, int N, int K, int bits, int group_size, void* stream)
+{
+    return qmv_affine_ex(w_packed, scales, biases, x, y, M, N, K, bits, group_size, QMV_DT_BF16,
+                         QMV_DT_BF16, QMV_DT_BF16, 0, stream);
+}
+
+int qmv_kernel_info(int M, int N, int K, int bits, int group_size, qmv_dtype x_dt,
+                    int rows_per_wave, qmv_kernel_info_t* out)
+{
+    if (!out) return QMV_E_NULL;
+    // validate the shape with stand-in aligned, non-overlapping pointers
+    const uintptr_t base = 1u << 20;
+    const uintptr_t stride = (uintptr_t)1 << 40;
+    int st = check_args(reinterpret_cast<const uint32_t*>(base), reinterpret_cast<const void*>(base + stride),
+                        reinterpret_cast<const void*>(base + 2 * stride), reinterpret_cast<const void*>(base + 3 * stride),
+                        reinterpret_cast<void*>(base + 4 * stride), M, N, K, bits, group_size, x_dt,
+                        QMV_DT_BF16, QMV_DT_F32, rows_per_wave);
+    if (st != QMV_OK) return st;
+    const bool xf32 = (x_dt == QMV_DT_F32);
+    const int mc = vectors_per_launch(M, N, K, bits, group_size, xf32, rows_per_wave);
+    if (mc < 1) return QMV_E_SHAPE;
+    const int R = rows_per_wave ? rows_per_wave : default_rows(mc, K / group_size, xf32);
+    Plan pl;
+    st = make_plan(mc, N, K, bits, group_size, xf32, R, pl);
+    if (st != QMV_OK) return st;
+    int nb = 0;
+    const int grid = plan_grid(pl, &nb);
+    if (grid < 1) return QMV_E_LAUNCH;
+    hipFuncAttributes attr;
+    if (hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(pl.fn)) != hipSuccess) return QMV_E_LAUNCH;
+    out->vgprs = attr.numRegs;
+    out->scratch_bytes = (int)attr.localSizeBytes;
+    out->lds_bytes = pl.lds;
+    out->wg_size = pl.W * qmv::kWave;
+    out->grid = grid;
+    out->waves_per_simd = nb * pl.W / 4;
+    out->rows_per_wave = R;
+    out->k_windows = pl.p.nwin;
+    return QMV_OK;
+}
+
+const char* qmv_status_string(int status)
+{
+    switch (status) {
+    case QMV_OK: return "QMV_OK";
+    case QMV_E_NULL: return "QMV_E_NULL";
+    case QMV_E_BITS: return "QMV_E_BITS";
+    case QMV_E_GROUP: return "QMV_E_GROUP";
+    case QMV_E_SHAPE: return "QMV_E_SHAPE";
+    case QMV_E_M_RANGE: return "QMV_E_M_RANGE";
+    case QMV_E_ALIGN: return "QMV_E_ALIGN";
+    case QMV_E_DTYPE: return "QMV_E_DTYPE";
+    case QMV_E_ROWS: return "QMV_E_ROWS";
+    case QMV_E_ALIAS: return "QMV_E_ALIAS";
+    case QMV_E_LAUNCH: return "QMV_E_LAUNCH";
+    default: return "QMV_E_UNKNOWN";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,6 @@
+// Kernel instances: 4-bit codes, groups of 64, f32 activations.
+#define QMV_BITS 4
+#define QMV_GS 64
+#define QMV_XF32 true
+#define QMV_TABLE qmv_table_b4_g64_f32
+#include "qmv_inst.inc"

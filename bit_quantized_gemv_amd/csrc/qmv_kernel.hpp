@@ -1,0 +1,597 @@
+// qmv_kernel.hpp -- gfx950 kernels of the affine group-quantized
+// matrix-vector product streamed over M <= 13 activation vectors.
+//
+//   y[m][n] = sum_g ( scale[n][g] * sum_{k in g} q[n][k] x[m][k]
+//                   + bias[n][g]  * sum_{k in g} x[m][k] )
+//
+// (mlxcel issue "an order-preserving streamed qmv would give MTP the fast
+// kernel and byte-identity together", sections "Correction to the obvious
+// sketch" and "Step 2"; mlxcel PR "block output rows per warp in qmv below
+// Ampere", sections "What lands" and "Not covered").
+//
+// Work decomposition
+//   * A row of packed weights is a sequence of 16-byte chunks.  Chunk c is read
+//     by lane c % 64 in wave step c / 64, so one wave-wide 128-bit load covers
+//     1 KiB of a row contiguously.
+//   * A wavefront owns R consecutive rows (row blocking): in a step it loads the
+//     chunk of each of its rows and reads the activations of that chunk from
+//     LDS once for all R rows.  A (row block, step) pair is a unit; each
+//     wavefront keeps the weights, scales and biases of the next PF units in
+//     flight (a register ring), so HBM sees several KiB per wavefront at once.
+//   * A workgroup of W wavefronts stages the activations x[0..M)[K-window] in
+//     LDS, together with the group sums S[m][g], and walks row blocks of W*R
+//     rows (persistent grid: staged once when the whole K fits).
+//   * The weight decode of a chunk happens once per step, outside the loop over
+//     the M vectors; every vector then reuses the decoded registers.
+//
+// Per-row arithmetic (fixed by K, bits, group size and activation dtype; it
+// never depends on M, R, W, the grid or the K-window size):
+//   1. bf16 activations: the chunk's codes become exact bf16 pairs
+//      (2^bits + q_a, 2^bits + q_b) -- the code sits in the top mantissa bits
+//      of a number in [2^bits, 2^(bits+1)) -- and D'_c is the chain of
+//      v_dot2_f32_bf16 over the chunk's pairs, from 0, in word order then pair
+//      order.  Pair j of a word holds fields (j, j + 32/(2 bits)); the matching
+//      activation pairs are laid out that way in LDS.
+//      fp32 activations: D'_c is the fma chain over the chunk's values in
+//      ascending k, from 0, with exact fp32 codes.
+//   2. The lpg = gs*bits/128 chunks of a group sit in adjacent lanes; their
+//      partials are combined by a DPP butterfly (xor 1, then xor 2).
+//   3. D = D' - 2^bits * S (bf16 path; exact offset removal up to one rounding),
+//      D = D' (fp32 path).  S[m][g] is the fp32 sum of the group's activations:
+//      8-value blocks summed left to right, blocks combined pairwise
+//      (xor-1, xor-2, ... tree).
+//   4. The group's owner lane (lane % lpg == step % lpg) folds once per group:
+//      acc = fma(scale, D, fma(bias, S, acc)), over its groups in ascending step.
+//   5. Row total: lanes l and l ^ d combined for d = 32, 16, 8, 4, 2, 1 in that
+//      order; then round-to-nearest-even to y's dtype.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+namespace qmv {
+
+constexpr int kWave = 64;
+constexpr int kMaxWaves = 8;
+constexpr int kLdsBytes = 163840;
+
+struct Params {
+    const uint32_t* w;
+    const uint16_t* s;
+    const uint16_t* b;
+    const void* x;
+    void* y;
+    int N;
+    int K;
+    int G;               // groups per row
+    int chunks;          // 16-byte weight chunks per row
+    int nsteps;          // wave steps per row, ceil(chunks / 64)
+    int win_steps;       // wave steps per K window
+    int nwin;            // K windows
+    int n_rb;            // row blocks of W*R rows
+    int sb_bf16;         // scales/biases: 1 = bf16, 0 = fp16
+    int y_bf16;          // y: 1 = bf16, 0 = fp32
+    int x_m_bytes;       // LDS bytes of one vector's activation window (padded)
+    int gw;              // groups per K window
+    int s_off;           // LDS offset of S[M][gw] (fp32)
+};
+
+// ------------------------------------------------------------------ helpers
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t h)
+{
+    return __half2float(__ushort_as_half(static_cast<unsigned short>(h)));
+}
+
+// IEEE round-to-nearest-even binary32 -> bfloat16 (NaN stays quiet NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// LDS activation layout: 16 bytes of padding after every 256 bytes, so that
+// 16 lanes reading 16-byte pieces at a 64/128/256-byte lane stride hit 64
+// distinct banks.
+__device__ __forceinline__ int lds_phys(int o) { return o + ((o >> 8) << 4); }
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141;
+constexpr int kRowMirror = 0x140;
+
+// Sum over the lanes of a group of n (1, 2, 4, 8 or 16) adjacent lanes; every
+// lane of the group ends with the same bits (each step adds two values that
+// the partner lane adds in the other order).
+template <int NL>
+__device__ __forceinline__ float lane_group_sum(float v)
+{
+    if constexpr (NL >= 2) v = v + dpp<kQuadXor1>(v);
+    if constexpr (NL >= 4) v = v + dpp<kQuadXor2>(v);
+    if constexpr (NL >= 8) v = v + dpp<kRowHalfMirror>(v);
+    if constexpr (NL >= 16) v = v + dpp<kRowMirror>(v);
+    return v;
+}
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c)
+{
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                           __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+// Exact bf16 pair (2^BITS + field j, 2^BITS + field j + 32/(2 BITS)) of a word.
+// 4-bit: 16 + q = 0x4180 | q << 3 (code in mantissa bits 3..6).
+// 2-bit:  4 + q = 0x4080 | q << 5 (code in mantissa bits 5..6).
+template <int BITS>
+__device__ __forceinline__ uint32_t code_pair(uint32_t w, int j)
+{
+    if constexpr (BITS == 4) {
+        const uint32_t t = (j == 0) ? (w << 3) : (w >> (4 * j - 3));
+        return (t & 0x00780078u) | 0x41804180u;
+    } else {
+        const int sh = 5 - 2 * j;
+        const uint32_t t = (sh >= 0) ? (w << sh) : (w >> (-sh));
+        return (t & 0x00600060u) | 0x40804080u;
+    }
+}
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 128-bit streaming load with the non-temporal hint (weights are read once).
+__device__ __forceinline__ uint4 load_nt(const uint4* p)
+{
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// ------------------------------------------------------ activation staging
+// Stages x[0..M)[window] into LDS (bf16 pairs in code-pair order, or fp32 in
+// natural order) and writes S[m][group] for the window's groups.
+template <int BITS, int GS, int M, bool XF32>
+__device__ void stage_x(const Params& p, uint8_t* lds, int win)
+{
+    constexpr int VPC = 128 / BITS;                      // values per 16-byte chunk
+    constexpr int UV = (!XF32 && BITS == 2) ? 16 : 8;    // values per staging unit
+    constexpr int UPG = GS / UV;                          // units per group
+    const int c_lo = win * p.win_steps * kWave;
+    const int c_hi = min(p.chunks, c_lo + p.win_steps * kWave);
+    const int k_lo = c_lo * VPC;
+    const int units_per_m = (c_hi - c_lo) * VPC / UV;
+    const int total = units_per_m * M;
+    float* S = reinterpret_cast<float*>(lds + p.s_off);
+
+    for (int base = 0; base < total; base += blockDim.x) {
+        const int u = base + threadIdx.x;
+        const bool valid = u < total;
+        const int m = valid ? u / units_per_m : 0;
+        const int l = valid ? u - m * units_per_m : 0;
+        const int k = k_lo + l * UV;
+        float part = 0.0f;
+        if constexpr (XF32) {
+            const float* xr = static_cast<const float*>(p.x) + (size_t)m * p.K + k;
+            float4 a = valid ? *reinterpret_cast<const float4*>(xr) : make_float4(0, 0, 0, 0);
+            float4 c = valid ? *reinterpret_cast<const float4*>(xr + 4) : make_float4(0, 0, 0, 0);
+            part = a.x; part = part + a.y; part = part + a.z; part = part + a.w;
+            part = part + c.x; part = part + c.y; part = part + c.z; part = part + c.w;
+            if (valid) {
+                uint8_t* dst = lds + m * p.x_m_bytes;
+                const int o = l * 32;
+                *reinterpret_cast<float4*>(dst + lds_phys(o)) = a;
+                *reinterpret_cast<float4*>(dst + lds_phys(o + 16)) = c;
+            }
+        } else {
+            const uint16_t* xr = static_cast<const uint16_t*>(p.x) + (size_t)m * p.K + k;
+            if constexpr (BITS == 4) {
+                uint4 d = valid ? *reinterpret_cast<const uint4*>(xr) : make_uint4(0, 0, 0, 0);
+                float v[8] = {bf16_bits_to_f32(d.x & 0xffffu), bf16_bits_to_f32(d.x >> 16),
+                              bf16_bits_to_f32(d.y & 0xffffu), bf16_bits_to_f32(d.y >> 16),
+                              bf16_bits_to_f32(d.z & 0xffffu), bf16_bits_to_f32(d.z >> 16),
+                              bf16_bits_to_f32(d.w & 0xffffu), bf16_bits_to_f32(d.w >> 16)};
+                part = v[0];
+#pragma unroll
+                for (int i = 1; i < 8; ++i) part = part + v[i];
+                if (valid) {
+                    // pairs (x_j, x_{j+4}), j = 0..3
+                    uint4 q;
+                    q.x = (d.x & 0xffffu) | (d.z << 16);
+                    q.y = (d.x >> 16) | (d.z & 0xffff0000u);
+                    q.z = (d.y & 0xffffu) | (d.w << 16);
+                    q.w = (d.y >> 16) | (d.w & 0xffff0000u);
+                    *reinterpret_cast<uint4*>(lds + m * p.x_m_bytes + lds_phys(l * 16)) = q;
+                }
+            } else {
+                uint4 d0 = valid ? *reinterpret_cast<const uint4*>(xr) : make_uint4(0, 0, 0, 0);
+                uint4 d1 = valid ? *reinterpret_cast<const uint4*>(xr + 8) : make_uint4(0, 0, 0, 0);
+                const uint32_t dw[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+                float pa = bf16_bits_to_f32(dw[0] & 0xffffu);
+                pa = pa + bf16_bits_to_f32(dw[0] >> 16);
+#pragma unroll
+                for (int i = 1; i < 4; ++i) {
+                    pa = pa + bf16_bits_to_f32(dw[i] & 0xffffu);
+                    pa = pa + bf16_bits_to_f32(dw[i] >> 16);
+                }
+                float pb = bf16_bits_to_f32(dw[4] & 0xffffu);
+                pb = pb + bf16_bits_to_f32(dw[4] >> 16);
+#pragma unroll
+                for (int i = 5; i < 8; ++i) {
+                    pb = pb + bf16_bits_to_f32(dw[i] & 0xffffu);
+                    pb = pb + bf16_bits_to_f32(dw[i] >> 16);
+                }
+                part = pa + pb;
+                if (valid) {
+                    // pairs (x_j, x_{j+8}), j = 0..7
+                    uint32_t pr[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const uint32_t lo = (j & 1) ? (dw[j >> 1] >> 16) : (dw[j >> 1] & 0xffffu);
+                        const uint32_t hi = (j & 1) ? (dw[4 + (j >> 1)] & 0xffff0000u)
+                                                    : (dw[4 + (j >> 1)] << 16);
+                        pr[j] = lo | hi;
+                    }
+                    uint8_t* dst = lds + m * p.x_m_bytes;
+                    *reinterpret_cast<uint4*>(dst + lds_phys(l * 32)) = make_uint4(pr[0], pr[1], pr[2], pr[3]);
+                    *reinterpret_cast<uint4*>(dst + lds_phys(l * 32 + 16)) = make_uint4(pr[4], pr[5], pr[6], pr[7]);
+                }
+            }
+        }
+        // group sum: the UPG units of a group sit in UPG adjacent lanes
+        part = lane_group_sum<UPG>(part);
+        if (valid && (l % UPG) == 0) S[m * p.gw + l / UPG] = part;
+    }
+}
+
+// --------------------------------------------------------- row reductions
+// Cross-lane exchange partner l ^ D for D in {1, 2, 4, 8}, within 16-lane rows.
+template <int D>
+__device__ __forceinline__ float xor_lanes(float v)
+{
+    const int i = __float_as_int(v);
+    if constexpr (D == 1) return __int_as_float(__builtin_amdgcn_update_dpp(0, i, kQuadXor1, 0xF, 0xF, false));
+    if constexpr (D == 2) return __int_as_float(__builtin_amdgcn_update_dpp(0, i, kQuadXor2, 0xF, 0xF, false));
+    // banks are the 4-lane quarters of a row; row_shl:n reads lane l + n, row_shr:n lane l - n
+    if constexpr (D == 4) {
+        int t = __builtin_amdgcn_update_dpp(0, i, 0x104, 0xF, 0x5, false);
+        return __int_as_float(__builtin_amdgcn_update_dpp(t, i, 0x114, 0xF, 0xA, false));
+    }
+    int t = __builtin_amdgcn_update_dpp(0, i, 0x108, 0xF, 0x3, false);
+    return __int_as_float(__builtin_amdgcn_update_dpp(t, i, 0x118, 0xF, 0xC, false));
+}
+
+constexpr int pow2_at_least(int v) { return v <= 1 ? 1 : 2 * pow2_at_least((v + 1) / 2); }
+
+// Row totals of V = R*M per-lane partials, all at once.  Every value is summed
+// over the 64 lanes by the same tree -- pairs of lanes l, l ^ d combined for
+// d = 32, 16, 8, 4, 2, 1 in that order -- so a value's bits do not depend on
+// how many other values share the reduction.  While several values remain per
+// lane, each level exchanges halves (permlane32/16 swaps, then DPP) so lane l
+// keeps a different value than lane l ^ d; once one value remains, the level
+// is a butterfly.  On return, v[0] of lane l holds the total of value
+// reduce_index<P>(l); lanes l with l % (64/P) == 0 hold distinct values.
+template <int P>
+__device__ __forceinline__ void lane_reduce(float (&v)[P], int lane)
+{
+    static_assert(P >= 1 && P <= 64 && (P & (P - 1)) == 0, "P must be a power of two <= 64");
+    // d = 32
+    if constexpr (P >= 2) {
+#pragma unroll
+        for (int i = 0; i < P / 2; ++i) {
+            auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[i]), __float_as_uint(v[i + P / 2]), false, false);
+            v[i] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+        }
+    } else {
+        auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[0]), __float_as_uint(v[0]), false, false);
+        v[0] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    }
+    // d = 16
+    if constexpr (P >= 4) {
+#pragma unroll
+        for (int i = 0; i < P / 4; ++i) {
+            auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[i]), __float_as_uint(v[i + P / 4]), false, false);
+            v[i] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+        }
+    } else {
+        auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[0]), __float_as_uint(v[0]), false, false);
+        v[0] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    }
+    // d = 8, 4, 2, 1
+    auto level = [&](auto dtag, auto ntag) {
+        constexpr int D = decltype(dtag)::value;
+        constexpr int NV = decltype(ntag)::value;   // values per lane before this level
+        if constexpr (NV >= 2) {
+            const bool hi = (lane & D) != 0;
+#pragma unroll
+            for (int i = 0; i < NV / 2; ++i) {
+                const float send = hi ? v[i] : v[i + NV / 2];
+                const float keep = hi ? v[i + NV / 2] : v[i];
+                v[i] = keep + xor_lanes<D>(send);
+            }
+        } else {
+            v[0] = v[0] + xor_lanes<D>(v[0]);
+        }
+    };
+    level(std::integral_constant<int, 8>{}, std::integral_constant<int, (P >= 8 ? P / 4 : 1)>{});
+    level(std::integral_constant<int, 4>{}, std::integral_constant<int, (P >= 16 ? P / 8 : 1)>{});
+    level(std::integral_constant<int, 2>{}, std::integral_constant<int, (P >= 32 ? P / 16 : 1)>{});
+    level(std::integral_constant<int, 1>{}, std::integral_constant<int, (P >= 64 ? P / 32 : 1)>{});
+}
+
+// Which value lane l holds after lane_reduce<P>.
+template <int P>
+__device__ __forceinline__ int reduce_index(int lane)
+{
+    int idx = 0, n = P;
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) {
+        if (n >= 2) {
+            if (lane & d) idx += n / 2;
+            n /= 2;
+        }
+    }
+    return idx;
+}
+
+// ------------------------------------------------------------------- kernel
+// Units in flight per wavefront (weight loads issued ahead of use).
+constexpr int prefetch_depth(int R, int M) { return (R * M <= 2) ? 4 : (R * M <= 8 ? 2 : 1); }
+
+template <int BITS, int GS, int R, int M, bool XF32>
+__global__ __launch_bounds__(kMaxWaves * kWave) void qmv_affine_kernel(const Params p)
+{
+    constexpr int LPG = GS * BITS / 128;          // lanes (chunks) per group
+    constexpr int VPC = 128 / BITS;               // values per chunk
+    constexpr int XCB = VPC * (XF32 ? 4 : 2);     // activation bytes per chunk in LDS
+    constexpr int OFFSET = 1 << BITS;             // code offset of the bf16 pairs
+    constexpr int PF = prefetch_depth(R, M);
+    constexpr int V = R * M;
+    constexpr int P = pow2_at_least(V);
+    static_assert(P <= 64, "R*M must not exceed 64");
+
+    extern __shared__ __align__(16) uint8_t lds[];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int W = blockDim.x / kWave;
+    const float* Slds = reinterpret_cast<const float*>(lds + p.s_off);
+    const int words_per_row = p.chunks * 4;
+
+    if ((int)blockIdx.x >= p.n_rb) return;
+    const int n_my = (p.n_rb - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+    const int n_units = n_my * p.nsteps;
+
+    // unit u of this wavefront: row block blockIdx.x + (u / nsteps) * gridDim.x, step u % nsteps
+    auto issue = [&](int u, uint4 (&wv)[R], uint32_t (&sv)[R], uint32_t (&bv)[R]) {
+        const int rbi = u / p.nsteps;
+        const int t = u - rbi * p.nsteps;
+        const int row0 = (((int)blockIdx.x + rbi * (int)gridDim.x) * W + wave) * R;
+        const int c = t * kWave + lane;
+        const bool active = c < p.chunks;
+        const int grp = c / LPG;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const bool ok = active && (row0 + r < p.N);
+            const size_t row = (size_t)(row0 + r);
+            wv[r] = ok ? load_nt(reinterpret_cast<const uint4*>(p.w + row * words_per_row) + c)
+                       : make_uint4(0, 0, 0, 0);
+            sv[r] = ok ? (uint32_t)p.s[row * p.G + grp] : 0u;
+            bv[r] = ok ? (uint32_t)p.b[row * p.G + grp] : 0u;
+        }
+    };
+
+    uint4 wb[PF][R];
+    uint32_t sb[PF][R], bb[PF][R];
+#pragma unroll
+    for (int s = 0; s < PF; ++s)
+        if (s < n_units) issue(s, wb[s], sb[s], bb[s]);
+
+    if (p.nwin == 1) {
+        stage_x<BITS, GS, M, XF32>(p, lds, 0);
+        __syncthreads();
+    }
+
+    float acc[R][M];
+    int t = 0, rbi = 0;
+    for (int ub = 0; ub < n_units; ub += PF) {
+#pragma unroll
+        for (int s = 0; s < PF; ++s) {
+            const int u = ub + s;
+            if (u < n_units) {
+                if (t == 0) {
+#pragma unroll
+                    for (int r = 0; r < R; ++r)
+#pragma unroll
+                        for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
+                }
+                if (p.nwin > 1 && (t % p.win_steps) == 0) {
+                    __syncthreads();
+                    stage_x<BITS, GS, M, XF32>(p, lds, t / p.win_steps);
+                    __syncthreads();
+                }
+                uint4 wcur[R];
+                float sv[R], bv[R];
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    wcur[r] = wb[s][r];
+                    sv[r] = p.sb_bf16 ? bf16_bits_to_f32(sb[s][r]) : f16_bits_to_f32(sb[s][r]);
+                    bv[r] = p.sb_bf16 ? bf16_bits_to_f32(bb[s][r]) : f16_bits_to_f32(bb[s][r]);
+                }
+                if (u + PF < n_units) issue(u + PF, wb[s], sb[s], bb[s]);
+
+                const int win = t / p.win_steps;
+                const int t_lo = win * p.win_steps;
+                const int c = t * kWave + lane;              // chunk of this lane
+                const bool active = c < p.chunks;
+                const int grp = active ? c / LPG : 0;        // group of the chunk
+                const int gl = active ? grp - win * p.gw : 0;  // group within the window
+                const bool owner = active && ((lane % LPG) == (t % LPG));
+                const int cl = c - t_lo * kWave;             // chunk within the window
+
+                if constexpr (!XF32) {
+                    // ---- bf16 activations: exact code pairs and v_dot2_f32_bf16
+                    constexpr int PPW = 16 / BITS;             // pairs per word
+                    constexpr int NH = (BITS == 4) ? 1 : 2;    // decode passes per chunk
+                    constexpr int WPH = 4 / NH;                // words per pass
+                    if constexpr (NH == 1) {
+                        uint32_t qp[R][4 * PPW];
+#pragma unroll
+                        for (int r = 0; r < R; ++r) {
+                            const uint32_t wd[4] = {wcur[r].x, wcur[r].y, wcur[r].z, wcur[r].w};
+#pragma unroll
+                            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                                for (int j = 0; j < PPW; ++j) qp[r][i * PPW + j] = code_pair<BITS>(wd[i], j);
+                        }
+#pragma unroll
+                        for (int m = 0; m < M; ++m) {
+                            const uint8_t* xs = lds + m * p.x_m_bytes;
+                            const float S = Slds[m * p.gw + gl];
+                            uint32_t xp[4 * PPW];
+#pragma unroll
+                            for (int v = 0; v < PPW; ++v) {
+                                const uint4 t4 = *reinterpret_cast<const uint4*>(xs + lds_phys(cl * XCB + v * 16));
+                                xp[4 * v + 0] = t4.x; xp[4 * v + 1] = t4.y;
+                                xp[4 * v + 2] = t4.z; xp[4 * v + 3] = t4.w;
+                            }
+#pragma unroll
+                            for (int r = 0; r < R; ++r) {
+                                float d = 0.0f;
+#pragma unroll
+                                for (int i = 0; i < 4 * PPW; ++i) d = dot2(qp[r][i], xp[i], d);
+                                d = lane_group_sum<LPG>(d);
+                                d = __builtin_fmaf(-(float)OFFSET, S, d);
+                                const float na = __builtin_fmaf(sv[r], d, __builtin_fmaf(bv[r], S, acc[r][m]));
+                                acc[r][m] = owner ? na : acc[r][m];
+                            }
+                        }
+                    } else {
+                        float dsum[R][M];
+#pragma unroll
+                        for (int h = 0; h < NH; ++h) {
+                            uint32_t qp[R][WPH * PPW];
+#pragma unroll
+                            for (int r = 0; r < R; ++r) {
+                                const uint32_t wd[4] = {wcur[r].x, wcur[r].y, wcur[r].z, wcur[r].w};
+#pragma unroll
+                                for (int i = 0; i < WPH; ++i)
+#pragma unroll
+                                    for (int j = 0; j < PPW; ++j)
+                                        qp[r][i * PPW + j] = code_pair<BITS>(wd[h * WPH + i], j);
+                            }
+#pragma unroll
+                            for (int m = 0; m < M; ++m) {
+                                const uint8_t* xs = lds + m * p.x_m_bytes;
+                                uint32_t xp[WPH * PPW];
+#pragma unroll
+                                for (int v = 0; v < WPH * PPW / 4; ++v) {
+                                    const uint4 t4 = *reinterpret_cast<const uint4*>(
+                                        xs + lds_phys(cl * XCB + h * (XCB / NH) + v * 16));
+                                    xp[4 * v + 0] = t4.x; xp[4 * v + 1] = t4.y;
+                                    xp[4 * v + 2] = t4.z; xp[4 * v + 3] = t4.w;
+                                }
+#pragma unroll
+                                for (int r = 0; r < R; ++r) {
+                                    float d = (h == 0) ? 0.0f : dsum[r][m];
+#pragma unroll
+                                    for (int i = 0; i < WPH * PPW; ++i) d = dot2(qp[r][i], xp[i], d);
+                                    dsum[r][m] = d;
+                                }
+                            }
+                        }
+#pragma unroll
+                        for (int m = 0; m < M; ++m) {
+                            const float S = Slds[m * p.gw + gl];
+#pragma unroll
+                            for (int r = 0; r < R; ++r) {
+                                float d = lane_group_sum<LPG>(dsum[r][m]);
+                                d = __builtin_fmaf(-(float)OFFSET, S, d);
+                                const float na = __builtin_fmaf(sv[r], d, __builtin_fmaf(bv[r], S, acc[r][m]));
+                                acc[r][m] = owner ? na : acc[r][m];
+                            }
+                        }
+                    }
+                } else {
+                    // ---- fp32 activations: exact fp32 codes and an fma chain
+                    constexpr int VPW = 32 / BITS;             // values per word
+                    float dsum[R][M];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        float qv[R][VPW];
+#pragma unroll
+                        for (int r = 0; r < R; ++r) {
+                            const uint32_t wd = (i == 0) ? wcur[r].x : (i == 1) ? wcur[r].y
+                                              : (i == 2) ? wcur[r].z : wcur[r].w;
+#pragma unroll
+                            for (int j = 0; j < VPW; ++j)
+                                qv[r][j] = (float)((wd >> (BITS * j)) & ((1u << BITS) - 1u));
+                        }
+#pragma unroll
+                        for (int m = 0; m < M; ++m) {
+                            const uint8_t* xs = lds + m * p.x_m_bytes;
+                            float xv[VPW];
+#pragma unroll
+                            for (int v = 0; v < VPW / 4; ++v) {
+                                const float4 t4 = *reinterpret_cast<const float4*>(
+                                    xs + lds_phys(cl * XCB + i * VPW * 4 + v * 16));
+                                xv[4 * v + 0] = t4.x; xv[4 * v + 1] = t4.y;
+                                xv[4 * v + 2] = t4.z; xv[4 * v + 3] = t4.w;
+                            }
+#pragma unroll
+                            for (int r = 0; r < R; ++r) {
+                                float d = (i == 0) ? 0.0f : dsum[r][m];
+#pragma unroll
+                                for (int j = 0; j < VPW; ++j) d = __builtin_fmaf(qv[r][j], xv[j], d);
+                                dsum[r][m] = d;
+                            }
+                        }
+                    }
+#pragma unroll
+                    for (int m = 0; m < M; ++m) {
+                        const float S = Slds[m * p.gw + gl];
+#pragma unroll
+                        for (int r = 0; r < R; ++r) {
+                            const float d = lane_group_sum<LPG>(dsum[r][m]);
+                            const float na = __builtin_fmaf(sv[r], d, __builtin_fmaf(bv[r], S, acc[r][m]));
+                            acc[r][m] = owner ? na : acc[r][m];
+                        }
+                    }
+                }
+
+                if (t == p.nsteps - 1) {
+                    // row totals and output: lane l stores value reduce_index(l)
+                    float v[P];
+#pragma unroll
+                    for (int i = 0; i < P; ++i) v[i] = (i < V) ? acc[i / M][i % M] : 0.0f;
+                    lane_reduce<P>(v, lane);
+                    const int idx = reduce_index<P>(lane);
+                    const int row0 = (((int)blockIdx.x + rbi * (int)gridDim.x) * W + wave) * R;
+                    const int r = idx / M, m = idx - (idx / M) * M;
+                    if ((lane % (64 / P)) == 0 && idx < V && row0 + r < p.N) {
+                        const size_t o = (size_t)m * p.N + row0 + r;
+                        if (p.y_bf16)
+                            static_cast<uint16_t*>(p.y)[o] = (uint16_t)f32_to_bf16_rne(v[0]);
+                        else
+                            static_cast<float*>(p.y)[o] = v[0];
+                    }
+                    t = 0;
+                    ++rbi;
+                } else {
+                    ++t;
+                }
+            }
+        }
+    }
+}
+
+}  // namespace qmv

@@ -1,0 +1,123 @@
+"""ctypes binding of the qmv C ABI (include/qmv.h).
+
+Argument marshalling only: every step of the product runs in the HIP kernels of
+lib/libqmv.so.  If the library has not been built this module raises -- there
+is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(PKG, "lib", "libqmv.so")
+
+DT_F32, DT_F16, DT_BF16 = 0, 1, 2
+MAX_M = 13
+
+
+class QmvError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} ({status})")
+
+
+class KernelInfo(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int) for n in ("vgprs", "scratch_bytes", "lds_bytes", "wg_size",
+                                             "grid", "waves_per_simd", "rows_per_wave",
+                                             "k_windows")]
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"HIP library {_LIB_PATH} is not built; run __graft_entry__.build()")
+        L = ctypes.CDLL(_LIB_PATH)
+        P, I = ctypes.c_void_p, ctypes.c_int
+        L.qmv_affine.argtypes = [P, P, P, P, P, I, I, I, I, I, P]
+        L.qmv_affine.restype = I
+        L.qmv_affine_ex.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, I, I, P]
+        L.qmv_affine_ex.restype = I
+        L.qmv_kernel_info.argtypes = [I, I, I, I, I, I, I, ctypes.POINTER(KernelInfo)]
+        L.qmv_kernel_info.restype = I
+        L.qmv_status_string.argtypes = [I]
+        L.qmv_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().qmv_status_string(status).decode()
+
+
+def affine_ptr(w, s, b, x, y, M, N, K, bits, group_size, x_dt=DT_BF16, sb_dt=DT_BF16,
+               y_dt=DT_BF16, rows_per_wave=0, stream=0) -> int:
+    """Raw C-ABI call with integer device pointers; returns the status code."""
+    return lib().qmv_affine_ex(w, s, b, x, y, M, N, K, bits, group_size, x_dt, sb_dt, y_dt,
+                               rows_per_wave, stream)
+
+
+def _dt_of(t, what):
+    import torch
+    if t.dtype == torch.float32:
+        return DT_F32
+    if t.dtype == torch.float16:
+        return DT_F16
+    if t.dtype == torch.bfloat16:
+        return DT_BF16
+    raise TypeError(f"{what}: unsupported dtype {t.dtype}")
+
+
+def affine(w, scales, biases, x, *, bits: int, group_size: int, out=None, out_dtype=None,
+           rows_per_wave: int = 0, stream=None):
+    """y[M][N] = qmv(x) on the current (or given) torch stream.
+
+    w: int32/uint32 [N][K*bits/32] packed codes (field 0 in the low bits);
+    scales, biases: fp16 or bf16 [N][K/group_size]; x: fp32 or bf16 [M][K]
+    (or [K]); out: optional fp32/bf16 [M][N] tensor, else allocated with
+    out_dtype (default bf16).
+    """
+    import torch
+    squeeze = x.dim() == 1
+    if squeeze:
+        x = x.unsqueeze(0)
+    for t, n in ((w, "w"), (scales, "scales"), (biases, "biases"), (x, "x")):
+        if not t.is_cuda:
+            raise ValueError(f"{n} must be a CUDA (HIP) tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{n} must be contiguous")
+    if w.dtype not in (torch.int32, torch.uint32):
+        raise TypeError("w must be int32 or uint32 packed words")
+    if scales.dtype != biases.dtype:
+        raise TypeError("scales and biases must share a dtype")
+    M, K = x.shape
+    N = w.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype or torch.bfloat16, device=x.device)
+    elif not out.is_contiguous() or tuple(out.shape) != (M, N):
+        raise ValueError("out must be a contiguous [M][N] tensor")
+    st = torch.cuda.current_stream(x.device) if stream is None else stream
+    status = affine_ptr(w.data_ptr(), scales.data_ptr(), biases.data_ptr(), x.data_ptr(),
+                        out.data_ptr(), M, N, K, bits, group_size, _dt_of(x, "x"),
+                        _dt_of(scales, "scales"), _dt_of(out, "out"), rows_per_wave,
+                        st.cuda_stream)
+    if status != 0:
+        raise QmvError(status, "qmv_affine_ex")
+    return out[0] if squeeze else out
+
+
+def kernel_info(M, N, K, bits, group_size, x_dt=DT_BF16, rows_per_wave=0) -> dict:
+    info = KernelInfo()
+    status = lib().qmv_kernel_info(M, N, K, bits, group_size, x_dt, rows_per_wave,
+                                   ctypes.byref(info))
+    if status != 0:
+        raise QmvError(status, "qmv_kernel_info")
+    return {n: getattr(info, n) for n, _ in KernelInfo._fields_}

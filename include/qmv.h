@@ -1,0 +1,139 @@
+/*
+ * qmv.h -- C ABI of the MI355X (gfx950) affine group-quantized
+ * matrix-vector product, streamed over up to 13 activation vectors.
+ *
+ * The operation.  For m < M and n < N,
+ *
+ *   y[m][n] = sum_{g < K/gs} ( scale[n][g] * sum_{k in g} q[n][k] * x[m][k]
+ *                            + bias[n][g]  * sum_{k in g} x[m][k] )
+ *
+ * i.e. the product of x with the affine-dequantized weights
+ * W[n][k] = scale[n][g(k)] * q[n][k] + bias[n][g(k)], with the group
+ * parameters applied once per group, to the raw integer dot and to sum(x).
+ * Defined in mlxcel issue "an order-preserving streamed qmv would give MTP the
+ * fast kernel and byte-identity together" (section "Correction to the obvious
+ * sketch: qdot does not dequantize": the qdot fold scale*accum + sum*bias) and
+ * mlxcel PR "block output rows per warp in qmv below Ampere" (section "Not
+ * covered": the per-group form).  The M vectors are those of a speculative /
+ * MTP verify block (same issue, sections "Problem" and "Scope limits").
+ *
+ * Layouts (all row-major, dense, no padding):
+ *   w_packed  uint32 [N][K*bits/32]; field j of a word (j < 32/bits) occupies
+ *             bits [bits*j, bits*(j+1)) -- field 0 in the low bits -- and
+ *             holds q[n][k] for k = word*(32/bits) + j.
+ *   scales, biases  [N][K/gs] of the parameter dtype (fp16 or bf16).
+ *   x         [M][K] of the activation dtype (fp32 or bf16).
+ *   y         [M][N] of the output dtype (fp32 or bf16), written with
+ *             round-to-nearest-even from the fp32 accumulator.
+ *
+ * Numerics.  Accumulation is fp32 in one fixed per-row order that depends on
+ * (K, bits, group_size, activation dtype) only: never on M, rows_per_wave, the
+ * launch shape or the stream.  Output vector m of an M-vector call is
+ * therefore bit-identical to a 1-vector call on x[m], and repeated calls are
+ * bit-identical.
+ *
+ * Ownership and concurrency.  Every pointer is device memory owned by the
+ * caller; the library never allocates, frees, or keeps a pointer past the
+ * call, and uses no workspace.  Inputs are read only; y must not overlap any
+ * input.  Calls are asynchronous on `stream` (a hipStream_t, NULL = the
+ * default stream): they return after the launch is enqueued and y is valid
+ * once the stream has been synchronized.  The only state the library keeps
+ * is a per-device cache of launch-shape queries (compute-unit count and
+ * occupancy per kernel instance), filled on first use under a lock;
+ * concurrent calls from several host threads are safe.  When one wave step
+ * of activations for all M vectors does not fit in LDS (fp32 activations with
+ * 2-bit codes and large M), a call is issued as several launches on the same
+ * stream, each over a subset of the vectors; the results do not change.
+ *
+ * Errors.  Arguments are validated on the host before anything is enqueued;
+ * on any non-zero status nothing was launched and y is untouched.  A HIP
+ * launch failure returns QMV_E_LAUNCH.  Faults inside a kernel surface, as
+ * with any HIP kernel, at the caller's next synchronization.
+ */
+#ifndef QMV_H
+#define QMV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { QMV_DT_F32 = 0, QMV_DT_F16 = 1, QMV_DT_BF16 = 2 } qmv_dtype;
+
+enum {
+    QMV_OK = 0,
+    QMV_E_NULL = 1,     /* a required pointer is NULL */
+    QMV_E_BITS = 2,     /* bits is not 2 or 4 */
+    QMV_E_GROUP = 3,    /* group_size is not 64 or 128 */
+    QMV_E_SHAPE = 4,    /* N < 1, K < 1, K % group_size != 0, or the shape exceeds
+                           the limits below */
+    QMV_E_M_RANGE = 5,  /* M is not in [1, QMV_MAX_M] */
+    QMV_E_ALIGN = 6,    /* w_packed, scales, biases or x is not 16-byte aligned, or y
+                           is not aligned to its element size */
+    QMV_E_DTYPE = 7,    /* unsupported dtype (x: f32/bf16; scales and biases:
+                           f16/bf16; y: f32/bf16) */
+    QMV_E_ROWS = 8,     /* rows_per_wave is not 0, 1, 2 or 4 */
+    QMV_E_ALIAS = 9,    /* y overlaps an input buffer */
+    QMV_E_LAUNCH = 10   /* the HIP runtime refused the launch (e.g. no gfx950 device) */
+};
+
+#define QMV_MAX_M 13
+/* Largest K (keeps every LDS and row offset inside 32-bit arithmetic). */
+#define QMV_MAX_K (1 << 20)
+#define QMV_MAX_N (1 << 28)
+
+/*
+ * y = qmv(x) with the common dtypes: x bf16, scales and biases bf16, y bf16.
+ *   w_packed, scales, biases, x, y: device pointers as laid out above.
+ *   M in [1, 13]; N >= 1; K >= group_size, K % group_size == 0;
+ *   bits in {2, 4}; group_size in {64, 128}; stream: hipStream_t or NULL.
+ * Returns QMV_OK or a QMV_E_* status.
+ */
+int qmv_affine(const uint32_t* w_packed, const void* scales, const void* biases,
+               const void* x, void* y, int M, int N, int K, int bits, int group_size,
+               void* stream);
+
+/*
+ * Same operation and kernel family with explicit dtypes and row blocking.
+ *   x_dt: QMV_DT_F32 or QMV_DT_BF16; sb_dt (scales and biases): QMV_DT_F16 or
+ *   QMV_DT_BF16; y_dt: QMV_DT_F32 or QMV_DT_BF16.
+ *   rows_per_wave: output rows owned by one wavefront (1, 2 or 4), or 0 for the
+ *   library's choice.  It changes the launch shape only, never the result
+ *   (mlxcel PR "block output rows per warp in qmv below Ampere", section "What
+ *   lands": row blocking leaves the per-row arithmetic untouched).
+ */
+int qmv_affine_ex(const uint32_t* w_packed, const void* scales, const void* biases,
+                  const void* x, void* y, int M, int N, int K, int bits, int group_size,
+                  qmv_dtype x_dt, qmv_dtype sb_dt, qmv_dtype y_dt, int rows_per_wave,
+                  void* stream);
+
+/* Resources and launch shape of the kernel the library would use for a call
+ * with these arguments (no launch is made; needs a gfx950 device for the
+ * occupancy query).  Fields: vgprs (architected VGPRs per lane as compiled),
+ * scratch_bytes (private memory per lane; 0 = no register spills), lds_bytes
+ * per workgroup (dynamic), wg_size (threads), grid (workgroups),
+ * waves_per_simd (resident waves per SIMD at this LDS/VGPR use), rows_per_wave,
+ * k_windows (K windows the activation tile is staged in; 1 = whole K). */
+typedef struct {
+    int vgprs;
+    int scratch_bytes;
+    int lds_bytes;
+    int wg_size;
+    int grid;
+    int waves_per_simd;
+    int rows_per_wave;
+    int k_windows;
+} qmv_kernel_info_t;
+
+int qmv_kernel_info(int M, int N, int K, int bits, int group_size, qmv_dtype x_dt,
+                    int rows_per_wave, qmv_kernel_info_t* out);
+
+/* Static string naming a status code ("QMV_OK", "QMV_E_BITS", ...). */
+const char* qmv_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QMV_H */

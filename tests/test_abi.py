@@ -1,0 +1,96 @@
+"""The C ABI library loads, exports every function include/qmv.h declares, and
+rejects bad arguments on the host before touching the GPU (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qmv.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(qmv_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    from bit_quantized_gemv_amd import qmv
+    if not os.path.exists(qmv.library_path()):
+        from bit_quantized_gemv_amd import build
+        build.build()
+    return qmv.lib()
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == ["qmv_affine", "qmv_affine_ex", "qmv_kernel_info",
+                                    "qmv_status_string"]
+
+
+def test_exports_every_declared_symbol(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_status_strings(L):
+    from bit_quantized_gemv_amd import qmv
+    names = ["QMV_OK", "QMV_E_NULL", "QMV_E_BITS", "QMV_E_GROUP", "QMV_E_SHAPE", "QMV_E_M_RANGE",
+             "QMV_E_ALIGN", "QMV_E_DTYPE", "QMV_E_ROWS", "QMV_E_ALIAS", "QMV_E_LAUNCH"]
+    for i, n in enumerate(names):
+        assert qmv.status_string(i) == n
+    assert qmv.status_string(99) == "QMV_E_UNKNOWN"
+    hdr = open(HEADER).read()
+    for i, n in enumerate(names):
+        assert re.search(rf"\b{n}\s*=\s*{i}\b", hdr), n
+
+
+# fake, 16-byte aligned, far-apart addresses: validation fails before any use
+A = 1 << 20
+S = 1 << 40
+W, SC, BI, X, Y = A, A + S, A + 2 * S, A + 3 * S, A + 4 * S
+GOOD = dict(M=1, N=256, K=512, bits=4, gs=64, xdt=2, sdt=2, ydt=2, R=0)
+
+
+def call(L, w=W, s=SC, b=BI, x=X, y=Y, **kw):
+    a = dict(GOOD)
+    a.update(kw)
+    return L.qmv_affine_ex(w, s, b, x, y, a["M"], a["N"], a["K"], a["bits"], a["gs"],
+                           a["xdt"], a["sdt"], a["ydt"], a["R"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(w=0), 1), (dict(s=0), 1), (dict(b=0), 1), (dict(x=0), 1), (dict(y=0), 1),
+    (dict(bits=3), 2), (dict(bits=8), 2), (dict(bits=1), 2),
+    (dict(gs=32), 3), (dict(gs=256), 3),
+    (dict(N=0), 4), (dict(N=-5), 4), (dict(K=0), 4), (dict(K=96), 4), (dict(K=32), 4),
+    (dict(K=(1 << 20) + 64), 4),
+    (dict(M=0), 5), (dict(M=14), 5), (dict(M=-1), 5),
+    (dict(w=W + 8), 6), (dict(s=SC + 4), 6), (dict(b=BI + 2), 6), (dict(x=X + 8), 6),
+    (dict(y=Y + 1), 6), (dict(y=Y + 2, ydt=0), 6),
+    (dict(xdt=1), 7), (dict(xdt=5), 7), (dict(sdt=0), 7), (dict(ydt=1), 7),
+    (dict(R=3), 8), (dict(R=8), 8), (dict(R=-1), 8),
+    (dict(y=X), 9), (dict(y=W + 64), 9), (dict(y=SC - 16), 9),
+])
+def test_rejects_bad_arguments(L, kw, code):
+    assert call(L, **kw) == code
+
+
+def test_kernel_info_validates(L):
+    from bit_quantized_gemv_amd import qmv
+    info = qmv.KernelInfo()
+    assert L.qmv_kernel_info(1, 256, 512, 3, 64, 2, 0, ctypes.byref(info)) == 2
+    assert L.qmv_kernel_info(14, 256, 512, 4, 64, 2, 0, ctypes.byref(info)) == 5
+    assert L.qmv_kernel_info(1, 256, 512, 4, 64, 2, 0, None) == 1
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    from bit_quantized_gemv_amd import qmv
+    w = torch.zeros(4, 64, dtype=torch.int32)
+    s = torch.zeros(4, 8, dtype=torch.bfloat16)
+    x = torch.zeros(1, 512, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        qmv.affine(w, s, s, x, bits=4, group_size=64)

@@ -1,0 +1,79 @@
+"""GPU invariants of the fixed per-row order: each output vector of an M-vector
+launch equals the 1-vector launch on that vector bit for bit, for every
+workload and M; rows per wavefront never change the bits; repeated runs are
+bit-identical; power-of-two scaling commutes exactly."""
+import numpy as np
+import pytest
+import torch
+
+import gpu_util as U
+from inputs import gen
+
+pytestmark = pytest.mark.gpu
+
+
+def _bits(t):
+    return t.contiguous().view(torch.int32 if t.dtype == torch.float32 else torch.int16)
+
+
+@pytest.mark.parametrize("name", list(gen.WORKLOADS))
+def test_m_invariance(name):
+    wl = gen.WORKLOADS[name]
+    p = gen.make_problem(name)
+    dev = U.to_dev(p)
+    ones = [U.gpu(p, dev, 1, torch.float32, x=dev[3][m:m + 1]) for m in range(13)]
+    for M in sorted(set(wl["Ms"]) | {2, 4, 5, 8, 10, 13}):
+        U.say(f"M-invariance {name} M={M}")
+        y = U.gpu(p, dev, M, torch.float32)
+        for m in range(M):
+            assert torch.equal(_bits(y[m]), _bits(ones[m][0])), f"{name}: M={M} vector {m}"
+        y16 = U.gpu(p, dev, M, torch.bfloat16)
+        for m in range(M):
+            assert torch.equal(_bits(y16[m]), _bits(U.rne_bf16(ones[m][0])))
+
+
+@pytest.mark.parametrize("name", ["up_4b_15360x3840", "down_4b_3840x15360", "up_2b_15360x3840",
+                                  "up_4b_17408x5120", "down_4b_5120x17408"])
+def test_rows_per_wave_invariance(name):
+    p = gen.make_problem(name)
+    dev = U.to_dev(p)
+    for M in (1, 5, 13):
+        U.say(f"R-invariance {name} M={M}")
+        ys = [U.gpu(p, dev, M, torch.float32, R=R) for R in (1, 2, 4)]
+        assert torch.equal(_bits(ys[0]), _bits(ys[1]))
+        assert torch.equal(_bits(ys[0]), _bits(ys[2]))
+
+
+def test_run_to_run_determinism():
+    p = gen.make_problem("up_4b_15360x3840")
+    dev = U.to_dev(p)
+    for M in (1, 13):
+        U.say(f"determinism M={M}")
+        y0 = U.gpu(p, dev, M, torch.float32)
+        for _ in range(10):
+            assert torch.equal(_bits(U.gpu(p, dev, M, torch.float32)), _bits(y0))
+
+
+@pytest.mark.parametrize("name", ["up_4b_15360x3840", "up_2b_15360x3840", "tiny_4b_g64"])
+def test_power_of_two_scaling_and_zero(name):
+    p = gen.make_problem(name)
+    dev = U.to_dev(p)
+    w, s, b, x = dev
+    U.say(f"scaling {name}")
+    y = U.gpu(p, dev, 5, torch.float32)
+    y2 = U.gpu(p, dev, 5, torch.float32, x=(x * 2).contiguous())
+    assert torch.equal(_bits(y2), _bits(y * 2))
+    z = U.gpu(p, dev, 3, torch.float32, x=torch.zeros_like(x))
+    assert not bool(z.any())
+    ys = U.gpu(p, (w, s * 2, b * 2, x), 4, torch.float32)
+    assert torch.equal(_bits(ys), _bits(U.gpu(p, dev, 4, torch.float32) * 2))
+
+
+def test_error_status_on_gpu():
+    import bit_quantized_gemv_amd as q
+    p = gen.make_problem("tiny_4b_g64")
+    w, s, b, x = U.to_dev(p)
+    with pytest.raises(q.QmvError):
+        q.affine(w, s, b, x[:13], bits=3, group_size=64)
+    with pytest.raises(q.QmvError):
+        q.affine(w, s, b, x[:5], bits=4, group_size=64, rows_per_wave=3)

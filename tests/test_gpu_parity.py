@@ -1,0 +1,145 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Small shapes span several wave steps, ragged step tails, ragged row blocks,
+K windows, single-group rows, N = 1, both code widths, both group sizes and all
+dtypes, compared element by element with the full oracle.  The full-size
+workloads are compared on sampled rows in the launch configuration the bench
+times.  The exact-integer and read-out cases must match bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gpu_util as U
+from inputs import gen
+from oracle import oracle
+
+pytestmark = pytest.mark.gpu
+
+SMALL = [  # N, K, bits, gs, sb, x, Ms
+    (67, 2560, 4, 64, "bf16", "bf16", (1, 3, 13)),    # 80 chunks: 1.25 wave steps
+    (67, 6400, 4, 64, "bf16", "bf16", (2, 13)),       # K windows at M = 13
+    (33, 512, 4, 128, "f16", "bf16", (1, 5)),
+    (130, 4608, 2, 128, "bf16", "bf16", (1, 5, 13)),  # 72 chunks
+    (45, 1024, 2, 64, "f16", "bf16", (2, 9)),
+    (256, 512, 4, 64, "f16", "f32", (1, 4)),          # the tiny workload's shape
+    (61, 2560, 2, 64, "bf16", "f32", (1, 7)),
+    (29, 1536, 4, 128, "bf16", "f32", (13,)),
+    (1, 128, 4, 64, "bf16", "bf16", (1, 13)),          # N = 1
+    (5, 64, 4, 64, "f16", "bf16", (1, 2)),             # one group per row
+    (3, 128, 2, 128, "bf16", "f32", (1, 3)),
+    (200, 8192, 2, 64, "bf16", "bf16", (6,)),          # 2 full wave steps at 2 bits
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: f"N{c[0]}_K{c[1]}_b{c[2]}_g{c[3]}_{c[4]}_{c[5]}")
+def test_small_vs_oracle(case):
+    N, K, bits, gs, sb, xdt, Ms = case
+    p = gen.make_problem(N=N, K=K, bits=bits, gs=gs, sb=sb, x_dtype=xdt, seed=N * 7 + K)
+    dev = U.to_dev(p)
+    for M in Ms:
+        U.say(f"case N={N} K={K} bits={bits} gs={gs} sb={sb} x={xdt} M={M}")
+        want = U.ref(p, M)
+        y32 = U.gpu(p, dev, M, torch.float32)
+        U.check_parity(y32, want, f"M={M}")
+        y16 = U.gpu(p, dev, M, torch.bfloat16)
+        assert torch.equal(y16.view(torch.int16), U.rne_bf16(y32).view(torch.int16))
+
+
+WORKLOADS = [n for n in gen.WORKLOADS if n != "tiny_4b_g64"]
+
+
+@pytest.mark.parametrize("name", WORKLOADS)
+def test_workload_vs_oracle_sampled(name):
+    wl = gen.WORKLOADS[name]
+    p = gen.make_problem(name)
+    dev = U.to_dev(p)
+    rng = np.random.default_rng(11)
+    rows = np.unique(np.concatenate([[0, 1, p.N - 1], rng.integers(0, p.N, 253)]))
+    for M in sorted(set((1,) + tuple(wl["Ms"]))):
+        U.say(f"workload {name} M={M}")
+        y32 = U.gpu(p, dev, M, torch.float32)
+        want = U.ref_rows(p, M, rows)
+        U.check_parity(y32[:, torch.from_numpy(rows).to(y32.device)], want, f"{name} M={M}")
+        y16 = U.gpu(p, dev, M, torch.bfloat16)
+        assert torch.equal(y16.view(torch.int16), U.rne_bf16(y32).view(torch.int16))
+        # the bf16 output is within one bf16 ulp of the rounded exact value
+        ref16 = torch.from_numpy(want).float().to(torch.bfloat16)
+        got16 = y16[:, torch.from_numpy(rows).to(y16.device)].cpu()
+        d = (got16.view(torch.int16).int() - ref16.view(torch.int16).int()).abs()
+        assert int(d.max()) <= 1
+
+
+def test_tiny_workload_full():
+    p = gen.make_problem("tiny_4b_g64")
+    dev = U.to_dev(p)
+    U.say("workload tiny_4b_g64 M=1")
+    U.check_parity(U.gpu(p, dev, 1, torch.float32), U.ref(p, 1), "tiny")
+
+
+def _exact_integer_problem(N, K, bits, gs, sb, xdt, seed):
+    """x in {-2..2}, scale = 2^-3, bias = -zp * 2^-3: every partial sum is an
+    exact multiple of 2^-3 far below 2^24, so any fp32 order gives the exact
+    value."""
+    p = gen.make_problem(N=N, K=K, bits=bits, gs=gs, sb=sb, x_dtype=xdt, seed=seed)
+    G = K // gs
+    zp = 8 if bits == 4 else 2
+    tdt = torch.float16 if sb == "f16" else torch.bfloat16
+    p.scales = torch.full((N, G), 0.125, dtype=tdt).view(torch.int16).numpy().view(np.uint16).copy()
+    p.biases = torch.full((N, G), -zp * 0.125, dtype=tdt).view(torch.int16).numpy().view(np.uint16).copy()
+    xi = np.random.default_rng(seed).integers(-2, 3, size=(13, K)).astype(np.float32)
+    p.x = xi if xdt == "f32" else torch.from_numpy(xi).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+    return p
+
+
+@pytest.mark.parametrize("case", [
+    (15360, 3840, 4, 64, "bf16", "bf16"), (3840, 15360, 4, 64, "bf16", "bf16"),
+    (15360, 3840, 2, 128, "bf16", "bf16"), (77, 2560, 4, 128, "f16", "f32"),
+    (91, 4608, 2, 64, "f16", "bf16"),
+], ids=lambda c: f"N{c[0]}_K{c[1]}_b{c[2]}_g{c[3]}_{c[5]}")
+def test_exact_integer_bit_exact(case):
+    N, K, bits, gs, sb, xdt = case
+    p = _exact_integer_problem(N, K, bits, gs, sb, xdt, seed=N + K)
+    dev = U.to_dev(p)
+    for M in (1, 13):
+        U.say(f"exact-integer N={N} K={K} bits={bits} gs={gs} M={M}")
+        y = U.gpu(p, dev, M, torch.float32).cpu().numpy().astype(np.float64)
+        if N * K * M <= 4e8:
+            want = U.ref(p, M)
+            assert np.array_equal(y, want)
+        else:
+            rows = np.arange(0, N, 97)
+            assert np.array_equal(y[:, rows], U.ref_rows(p, M, rows))
+
+
+@pytest.mark.parametrize("bits,gs", [(4, 64), (4, 128), (2, 64), (2, 128)])
+def test_readout_e_k(bits, gs):
+    """scale 1, bias 0, x = e_k: y[m][n] = q[n][k_m] exactly, with q the
+    generator's codes before packing."""
+    N, K = 37, 8192
+    wp, _, _, qc = gen.make_weights(N, K, bits, gs, "bf16", seed=5 + bits + gs, keep_q=True)
+    G = K // gs
+    ks = [0, 1, 31, 32, 63, 64, 2047, 2048, 4095, 4096, 6000, 8190, 8191]
+    x = np.zeros((13, K), dtype=np.float32)
+    x[np.arange(13), ks] = 1.0
+    w = torch.from_numpy(wp.view(np.int32)).to(U.DEV)
+    one = torch.ones(N, G, dtype=torch.bfloat16, device=U.DEV)
+    zero = torch.zeros(N, G, dtype=torch.bfloat16, device=U.DEV)
+    import bit_quantized_gemv_amd as q
+    for xdt in ("bf16", "f32"):
+        U.say(f"read-out bits={bits} gs={gs} x={xdt}")
+        xd = U.x_to_dev(x if xdt == "f32" else torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16), xdt)
+        y = q.affine(w, one, zero, xd, bits=bits, group_size=gs, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert np.array_equal(y.cpu().numpy(), qc[:, ks].T.astype(np.float32))
+
+
+def test_subnormal_fp16_scales():
+    """fp16 parameters convert exactly, subnormals included."""
+    N, K = 64, 1024
+    p = gen.make_problem(N=N, K=K, bits=4, gs=64, sb="f16", x_dtype="f32", seed=3)
+    p.scales = p.scales.copy()
+    p.scales[:, ::3] = np.arange(1, 1 + p.scales[:, ::3].size, dtype=np.uint16).reshape(p.scales[:, ::3].shape) % 1023 + 1
+    dev = U.to_dev(p)
+    U.say("fp16 subnormal scales")
+    U.check_parity(U.gpu(p, dev, 3), U.ref(p, 3), "subnormal scales")
