@@ -58,14 +58,15 @@ int check_args(const uint32_t* w, const void* s, const void* b, const void* x, v
     return QMV_OK;
 }
 
-KernelFn pick_kernel(int bits, int gs, bool xf32, int R, int M)
+KernelFn pick_kernel(int bits, int gs, bool xf32, bool sbf, int R, int M)
 {
     const int ri = r_index(R);
     const int mi = M - 1;
-    if (bits == 4 && gs == 64) return xf32 ? qmv::qmv_table_b4_g64_f32[ri][mi] : qmv::qmv_table_b4_g64_bf16[ri][mi];
-    if (bits == 4 && gs == 128) return xf32 ? qmv::qmv_table_b4_g128_f32[ri][mi] : qmv::qmv_table_b4_g128_bf16[ri][mi];
-    if (bits == 2 && gs == 64) return xf32 ? qmv::qmv_table_b2_g64_f32[ri][mi] : qmv::qmv_table_b2_g64_bf16[ri][mi];
-    return xf32 ? qmv::qmv_table_b2_g128_f32[ri][mi] : qmv::qmv_table_b2_g128_bf16[ri][mi];
+    const int si = sbf ? 1 : 0;
+    if (bits == 4 && gs == 64) return xf32 ? qmv::qmv_table_b4_g64_f32[ri][mi][si] : qmv::qmv_table_b4_g64_bf16[ri][mi][si];
+    if (bits == 4 && gs == 128) return xf32 ? qmv::qmv_table_b4_g128_f32[ri][mi][si] : qmv::qmv_table_b4_g128_bf16[ri][mi][si];
+    if (bits == 2 && gs == 64) return xf32 ? qmv::qmv_table_b2_g64_f32[ri][mi][si] : qmv::qmv_table_b2_g64_bf16[ri][mi][si];
+    return xf32 ? qmv::qmv_table_b2_g128_f32[ri][mi][si] : qmv::qmv_table_b2_g128_bf16[ri][mi][si];
 }
 
 // Library choice of rows per wavefront.
@@ -85,7 +86,7 @@ struct Plan {
 
 // LDS layout and K windows.  Returns QMV_E_SHAPE if one wave step of
 // activations for all M vectors does not fit in LDS.
-int make_plan(int M, int N, int K, int bits, int gs, bool xf32, int R, Plan& pl)
+int make_plan(int M, int N, int K, int bits, int gs, bool xf32, bool sbf, int R, Plan& pl)
 {
     const int G = K / gs;
     const int lpg = gs * bits / 128;
@@ -125,7 +126,7 @@ int make_plan(int M, int N, int K, int bits, int gs, bool xf32, int R, Plan& pl)
     pl.lds = p.s_off + ((s_bytes + 15) / 16) * 16;
     pl.R = R;
     pl.W = W;
-    pl.fn = pick_kernel(bits, gs, xf32, R, M);
+    pl.fn = pick_kernel(bits, gs, xf32, sbf, R, M);
     return QMV_OK;
 }
 
@@ -196,7 +197,7 @@ int vectors_per_launch(int M, int N, int K, int bits, int gs, bool xf32, int R_r
     for (int mc = M; mc >= 1; --mc) {
         Plan pl;
         const int R = R_req ? R_req : default_rows(mc, K / gs, xf32);
-        if (make_plan(mc, N, K, bits, gs, xf32, R, pl) == QMV_OK) return mc;
+        if (make_plan(mc, N, K, bits, gs, xf32, true, R, pl) == QMV_OK) return mc;
     }
     return 0;
 }
@@ -221,7 +222,7 @@ int qmv_affine_ex(const uint32_t* w_packed, const void* scales, const void* bias
         const int mm = std::min(mc, M - m0);
         const int R = rows_per_wave ? rows_per_wave : default_rows(mm, G, xf32);
         Plan pl;
-        st = make_plan(mm, N, K, bits, group_size, xf32, R, pl);
+        st = make_plan(mm, N, K, bits, group_size, xf32, sb_dt == QMV_DT_BF16, R, pl);
         if (st != QMV_OK) return st;
         Params& p = pl.p;
         p.w = w_packed;
@@ -229,7 +230,6 @@ int qmv_affine_ex(const uint32_t* w_packed, const void* scales, const void* bias
         p.b = static_cast<const uint16_t*>(biases);
         p.x = static_cast<const uint8_t*>(x) + (size_t)m0 * K * dtype_bytes(x_dt);
         p.y = static_cast<uint8_t*>(y) + (size_t)m0 * N * dtype_bytes(y_dt);
-        p.sb_bf16 = (sb_dt == QMV_DT_BF16);
         p.y_bf16 = (y_dt == QMV_DT_BF16);
         const int grid = plan_grid(pl, nullptr);
         if (grid < 1) return QMV_E_LAUNCH;
@@ -266,7 +266,7 @@ int qmv_kernel_info(int M, int N, int K, int bits, int group_size, qmv_dtype x_d
     if (mc < 1) return QMV_E_SHAPE;
     const int R = rows_per_wave ? rows_per_wave : default_rows(mc, K / group_size, xf32);
     Plan pl;
-    st = make_plan(mc, N, K, bits, group_size, xf32, R, pl);
+    st = make_plan(mc, N, K, bits, group_size, xf32, true, R, pl);
     if (st != QMV_OK) return st;
     int nb = 0;
     const int grid = plan_grid(pl, &nb);

@@ -9,14 +9,15 @@ namespace qmv {
 using KernelFn = void (*)(Params);
 constexpr int kNumR = 3;      // rows per wavefront 1, 2, 4
 constexpr int kMaxM = 13;
+constexpr int kNumSb = 2;     // scales/biases fp16, bf16
 
-extern const KernelFn qmv_table_b4_g64_bf16[kNumR][kMaxM];
-extern const KernelFn qmv_table_b4_g64_f32[kNumR][kMaxM];
-extern const KernelFn qmv_table_b4_g128_bf16[kNumR][kMaxM];
-extern const KernelFn qmv_table_b4_g128_f32[kNumR][kMaxM];
-extern const KernelFn qmv_table_b2_g64_bf16[kNumR][kMaxM];
-extern const KernelFn qmv_table_b2_g64_f32[kNumR][kMaxM];
-extern const KernelFn qmv_table_b2_g128_bf16[kNumR][kMaxM];
-extern const KernelFn qmv_table_b2_g128_f32[kNumR][kMaxM];
+extern const KernelFn qmv_table_b4_g64_bf16[kNumR][kMaxM][kNumSb];
+extern const KernelFn qmv_table_b4_g64_f32[kNumR][kMaxM][kNumSb];
+extern const KernelFn qmv_table_b4_g128_bf16[kNumR][kMaxM][kNumSb];
+extern const KernelFn qmv_table_b4_g128_f32[kNumR][kMaxM][kNumSb];
+extern const KernelFn qmv_table_b2_g64_bf16[kNumR][kMaxM][kNumSb];
+extern const KernelFn qmv_table_b2_g64_f32[kNumR][kMaxM][kNumSb];
+extern const KernelFn qmv_table_b2_g128_bf16[kNumR][kMaxM][kNumSb];
+extern const KernelFn qmv_table_b2_g128_f32[kNumR][kMaxM][kNumSb];
 
 }  // namespace qmv

@@ -72,7 +72,6 @@ struct Params {
     int win_steps;       // wave steps per K window
     int nwin;            // K windows
     int n_rb;            // row blocks of W*R rows
-    int sb_bf16;         // scales/biases: 1 = bf16, 0 = fp16
     int y_bf16;          // y: 1 = bf16, 0 = fp32
     int x_m_bytes;       // LDS bytes of one vector's activation window (padded)
     int gw;              // groups per K window
@@ -133,126 +132,220 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c)
                                            __builtin_bit_cast(bf16x2, b), c, false);
 }
 
+// (a & mask) | magic in one v_and_or_b32.  gfx9 VALU instructions read at
+// most one scalar operand, so the mask rides in an SGPR and the magic in a
+// VGPR (the compiler would otherwise split this into v_and + v_or).
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t magic)
+{
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(mask), "v"(magic));
+    return r;
+}
+
+template <int BITS>
+constexpr uint32_t code_magic() { return BITS == 4 ? 0x41804180u : 0x40804080u; }
+
 // Exact bf16 pair (2^BITS + field j, 2^BITS + field j + 32/(2 BITS)) of a word.
 // 4-bit: 16 + q = 0x4180 | q << 3 (code in mantissa bits 3..6).
 // 2-bit:  4 + q = 0x4080 | q << 5 (code in mantissa bits 5..6).
+// `magic` is code_magic<BITS>() held in a VGPR.
 template <int BITS>
-__device__ __forceinline__ uint32_t code_pair(uint32_t w, int j)
+__device__ __forceinline__ uint32_t code_pair(uint32_t w, int j, uint32_t magic)
 {
     if constexpr (BITS == 4) {
         const uint32_t t = (j == 0) ? (w << 3) : (w >> (4 * j - 3));
-        return (t & 0x00780078u) | 0x41804180u;
+        return and_or(t, 0x00780078u, magic);
     } else {
         const int sh = 5 - 2 * j;
         const uint32_t t = (sh >= 0) ? (w << sh) : (w >> (-sh));
-        return (t & 0x00600060u) | 0x40804080u;
+        return and_or(t, 0x00600060u, magic);
     }
 }
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+// Buffer resources.  Loads go through raw buffer instructions: an offset at or
+// past num_records returns zero without touching memory, so masked lanes need
+// no branch and the compiler can count outstanding loads exactly.
+constexpr uint32_t kRsrcWord3 = 0x00020000u;   // gfx9-family raw buffer
+constexpr int kOut = 0x7ffffff0;               // an offset past any record count
 
-// 128-bit streaming load with the non-temporal hint (weights are read once).
-__device__ __forceinline__ uint4 load_nt(const uint4* p)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, long long bytes)
 {
-    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-    return make_uint4(v.x, v.y, v.z, v.w);
+    const long long n = bytes <= 0 ? 0 : (bytes > 0xffffffffll ? 0xffffffffll : bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)(uint32_t)n,
+                                             (int)kRsrcWord3);
+}
+
+// 128-bit load with the non-temporal hint (weights are streamed once).
+__device__ __forceinline__ uint4 buf_load_nt(__amdgpu_buffer_rsrc_t r, int off)
+{
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+__device__ __forceinline__ uint4 buf_load(__amdgpu_buffer_rsrc_t r, int off)
+{
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// Hides how an offset was computed, so the compiler keeps one unconditional
+// load instead of re-splitting a masked offset into guarded branches.
+__device__ __forceinline__ int opaque(int v)
+{
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
+__device__ __forceinline__ uint16_t buf_load_u16(__amdgpu_buffer_rsrc_t r, int off)
+{
+    return (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
 }
 
 // ------------------------------------------------------ activation staging
 // Stages x[0..M)[window] into LDS (bf16 pairs in code-pair order, or fp32 in
-// natural order) and writes S[m][group] for the window's groups.
+// natural order) and writes S[m][group] for the window's groups.  Work is cut
+// into rounds of blockDim units (a unit = UV consecutive values of one vector);
+// load() issues a round's loads, store() consumes them, so the first round's
+// loads can be issued ahead of the weight stream.
 template <int BITS, int GS, int M, bool XF32>
-__device__ void stage_x(const Params& p, uint8_t* lds, int win)
-{
-    constexpr int VPC = 128 / BITS;                      // values per 16-byte chunk
-    constexpr int UV = (!XF32 && BITS == 2) ? 16 : 8;    // values per staging unit
-    constexpr int UPG = GS / UV;                          // units per group
-    const int c_lo = win * p.win_steps * kWave;
-    const int c_hi = min(p.chunks, c_lo + p.win_steps * kWave);
-    const int k_lo = c_lo * VPC;
-    const int units_per_m = (c_hi - c_lo) * VPC / UV;
-    const int total = units_per_m * M;
-    float* S = reinterpret_cast<float*>(lds + p.s_off);
+struct Stager {
+    static constexpr int VPC = 128 / BITS;                    // values per weight chunk
+    static constexpr int UV = (!XF32 && BITS == 2) ? 16 : 8;  // values per unit
+    static constexpr int UPG = GS / UV;                       // units per group
+    static constexpr int NLD = (XF32 || BITS == 2) ? 2 : 1;   // 16-byte loads per unit
+    static constexpr int NRB = (M >= 8) ? 8 : (M >= 3 ? 4 : 2);  // rounds whose loads are in flight together
 
-    for (int base = 0; base < total; base += blockDim.x) {
-        const int u = base + threadIdx.x;
-        const bool valid = u < total;
-        const int m = valid ? u / units_per_m : 0;
-        const int l = valid ? u - m * units_per_m : 0;
-        const int k = k_lo + l * UV;
-        float part = 0.0f;
+    int units_per_m, total, rounds, k_lo;
+
+    __device__ void begin(const Params& p, int win)
+    {
+        const int c_lo = win * p.win_steps * kWave;
+        const int c_hi = min(p.chunks, c_lo + p.win_steps * kWave);
+        units_per_m = (c_hi - c_lo) * VPC / UV;
+        total = units_per_m * M;
+        rounds = (total + (int)blockDim.x - 1) / (int)blockDim.x;
+        k_lo = c_lo * VPC;
+    }
+
+    // unit handled by this thread in round `round`
+    __device__ void where(int round, int& m, int& l, bool& valid) const
+    {
+        const int u = round * (int)blockDim.x + (int)threadIdx.x;
+        valid = u < total;
+        m = valid ? u / units_per_m : 0;
+        l = valid ? u - m * units_per_m : 0;
+    }
+
+    // issue the loads of one round (all threads issue; masked lanes read nothing)
+    __device__ void load(const Params& p, __amdgpu_buffer_rsrc_t xr, int round, uint4 (&d)[NLD]) const
+    {
+        int m, l;
+        bool valid;
+        where(round, m, l, valid);
+        const int off = opaque(valid ? (m * p.K + k_lo + l * UV) * (XF32 ? 4 : 2) : kOut);
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) d[i] = buf_load(xr, off + 16 * i);
+    }
+
+    __device__ void store(const Params& p, uint8_t* lds, int round, const uint4 (&d)[NLD]) const
+    {
+        int m, l;
+        bool valid;
+        where(round, m, l, valid);
+        float* S = reinterpret_cast<float*>(lds + p.s_off);
+        uint8_t* dst = lds + m * p.x_m_bytes;
+        float part;
         if constexpr (XF32) {
-            const float* xr = static_cast<const float*>(p.x) + (size_t)m * p.K + k;
-            float4 a = valid ? *reinterpret_cast<const float4*>(xr) : make_float4(0, 0, 0, 0);
-            float4 c = valid ? *reinterpret_cast<const float4*>(xr + 4) : make_float4(0, 0, 0, 0);
-            part = a.x; part = part + a.y; part = part + a.z; part = part + a.w;
-            part = part + c.x; part = part + c.y; part = part + c.z; part = part + c.w;
+            const float v[8] = {__uint_as_float(d[0].x), __uint_as_float(d[0].y),
+                                __uint_as_float(d[0].z), __uint_as_float(d[0].w),
+                                __uint_as_float(d[1].x), __uint_as_float(d[1].y),
+                                __uint_as_float(d[1].z), __uint_as_float(d[1].w)};
+            part = v[0];
+#pragma unroll
+            for (int i = 1; i < 8; ++i) part = part + v[i];
             if (valid) {
-                uint8_t* dst = lds + m * p.x_m_bytes;
-                const int o = l * 32;
-                *reinterpret_cast<float4*>(dst + lds_phys(o)) = a;
-                *reinterpret_cast<float4*>(dst + lds_phys(o + 16)) = c;
+                *reinterpret_cast<uint4*>(dst + lds_phys(l * 32)) = d[0];
+                *reinterpret_cast<uint4*>(dst + lds_phys(l * 32 + 16)) = d[1];
+            }
+        } else if constexpr (BITS == 4) {
+            const uint4 q0 = d[0];
+            const float v[8] = {bf16_bits_to_f32(q0.x & 0xffffu), bf16_bits_to_f32(q0.x >> 16),
+                                bf16_bits_to_f32(q0.y & 0xffffu), bf16_bits_to_f32(q0.y >> 16),
+                                bf16_bits_to_f32(q0.z & 0xffffu), bf16_bits_to_f32(q0.z >> 16),
+                                bf16_bits_to_f32(q0.w & 0xffffu), bf16_bits_to_f32(q0.w >> 16)};
+            part = v[0];
+#pragma unroll
+            for (int i = 1; i < 8; ++i) part = part + v[i];
+            if (valid) {
+                // pairs (x_j, x_{j+4}), j = 0..3
+                uint4 q;
+                q.x = (q0.x & 0xffffu) | (q0.z << 16);
+                q.y = (q0.x >> 16) | (q0.z & 0xffff0000u);
+                q.z = (q0.y & 0xffffu) | (q0.w << 16);
+                q.w = (q0.y >> 16) | (q0.w & 0xffff0000u);
+                *reinterpret_cast<uint4*>(dst + lds_phys(l * 16)) = q;
             }
         } else {
-            const uint16_t* xr = static_cast<const uint16_t*>(p.x) + (size_t)m * p.K + k;
-            if constexpr (BITS == 4) {
-                uint4 d = valid ? *reinterpret_cast<const uint4*>(xr) : make_uint4(0, 0, 0, 0);
-                float v[8] = {bf16_bits_to_f32(d.x & 0xffffu), bf16_bits_to_f32(d.x >> 16),
-                              bf16_bits_to_f32(d.y & 0xffffu), bf16_bits_to_f32(d.y >> 16),
-                              bf16_bits_to_f32(d.z & 0xffffu), bf16_bits_to_f32(d.z >> 16),
-                              bf16_bits_to_f32(d.w & 0xffffu), bf16_bits_to_f32(d.w >> 16)};
-                part = v[0];
+            const uint32_t dw[8] = {d[0].x, d[0].y, d[0].z, d[0].w, d[1].x, d[1].y, d[1].z, d[1].w};
+            float pa = bf16_bits_to_f32(dw[0] & 0xffffu);
+            pa = pa + bf16_bits_to_f32(dw[0] >> 16);
 #pragma unroll
-                for (int i = 1; i < 8; ++i) part = part + v[i];
-                if (valid) {
-                    // pairs (x_j, x_{j+4}), j = 0..3
-                    uint4 q;
-                    q.x = (d.x & 0xffffu) | (d.z << 16);
-                    q.y = (d.x >> 16) | (d.z & 0xffff0000u);
-                    q.z = (d.y & 0xffffu) | (d.w << 16);
-                    q.w = (d.y >> 16) | (d.w & 0xffff0000u);
-                    *reinterpret_cast<uint4*>(lds + m * p.x_m_bytes + lds_phys(l * 16)) = q;
-                }
-            } else {
-                uint4 d0 = valid ? *reinterpret_cast<const uint4*>(xr) : make_uint4(0, 0, 0, 0);
-                uint4 d1 = valid ? *reinterpret_cast<const uint4*>(xr + 8) : make_uint4(0, 0, 0, 0);
-                const uint32_t dw[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
-                float pa = bf16_bits_to_f32(dw[0] & 0xffffu);
-                pa = pa + bf16_bits_to_f32(dw[0] >> 16);
+            for (int i = 1; i < 4; ++i) {
+                pa = pa + bf16_bits_to_f32(dw[i] & 0xffffu);
+                pa = pa + bf16_bits_to_f32(dw[i] >> 16);
+            }
+            float pb = bf16_bits_to_f32(dw[4] & 0xffffu);
+            pb = pb + bf16_bits_to_f32(dw[4] >> 16);
 #pragma unroll
-                for (int i = 1; i < 4; ++i) {
-                    pa = pa + bf16_bits_to_f32(dw[i] & 0xffffu);
-                    pa = pa + bf16_bits_to_f32(dw[i] >> 16);
-                }
-                float pb = bf16_bits_to_f32(dw[4] & 0xffffu);
-                pb = pb + bf16_bits_to_f32(dw[4] >> 16);
+            for (int i = 5; i < 8; ++i) {
+                pb = pb + bf16_bits_to_f32(dw[i] & 0xffffu);
+                pb = pb + bf16_bits_to_f32(dw[i] >> 16);
+            }
+            part = pa + pb;
+            if (valid) {
+                // pairs (x_j, x_{j+8}), j = 0..7
+                uint32_t pr[8];
 #pragma unroll
-                for (int i = 5; i < 8; ++i) {
-                    pb = pb + bf16_bits_to_f32(dw[i] & 0xffffu);
-                    pb = pb + bf16_bits_to_f32(dw[i] >> 16);
+                for (int j = 0; j < 8; ++j) {
+                    const uint32_t lo = (j & 1) ? (dw[j >> 1] >> 16) : (dw[j >> 1] & 0xffffu);
+                    const uint32_t hi = (j & 1) ? (dw[4 + (j >> 1)] & 0xffff0000u) : (dw[4 + (j >> 1)] << 16);
+                    pr[j] = lo | hi;
                 }
-                part = pa + pb;
-                if (valid) {
-                    // pairs (x_j, x_{j+8}), j = 0..7
-                    uint32_t pr[8];
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        const uint32_t lo = (j & 1) ? (dw[j >> 1] >> 16) : (dw[j >> 1] & 0xffffu);
-                        const uint32_t hi = (j & 1) ? (dw[4 + (j >> 1)] & 0xffff0000u)
-                                                    : (dw[4 + (j >> 1)] << 16);
-                        pr[j] = lo | hi;
-                    }
-                    uint8_t* dst = lds + m * p.x_m_bytes;
-                    *reinterpret_cast<uint4*>(dst + lds_phys(l * 32)) = make_uint4(pr[0], pr[1], pr[2], pr[3]);
-                    *reinterpret_cast<uint4*>(dst + lds_phys(l * 32 + 16)) = make_uint4(pr[4], pr[5], pr[6], pr[7]);
-                }
+                *reinterpret_cast<uint4*>(dst + lds_phys(l * 32)) = make_uint4(pr[0], pr[1], pr[2], pr[3]);
+                *reinterpret_cast<uint4*>(dst + lds_phys(l * 32 + 16)) = make_uint4(pr[4], pr[5], pr[6], pr[7]);
             }
         }
         // group sum: the UPG units of a group sit in UPG adjacent lanes
         part = lane_group_sum<UPG>(part);
         if (valid && (l % UPG) == 0) S[m * p.gw + l / UPG] = part;
     }
-}
+
+    // Stage a window: the loads of up to NRB rounds are issued together, then
+    // stored.  `between` runs after the first batch's loads are issued (the
+    // caller issues its weight prefetch there, so both streams overlap).
+    template <class F>
+    __device__ void stage(const Params& p, __amdgpu_buffer_rsrc_t xr, uint8_t* lds, int win, F&& between)
+    {
+        begin(p, win);
+        {
+            uint4 d[NRB][NLD];
+#pragma unroll
+            for (int i = 0; i < NRB; ++i) load(p, xr, i, d[i]);
+            between();
+#pragma unroll
+            for (int i = 0; i < NRB; ++i)
+                if (i < rounds) store(p, lds, i, d[i]);
+        }
+        for (int r0 = NRB; r0 < rounds; r0 += NRB) {
+            uint4 d[NRB][NLD];
+#pragma unroll
+            for (int i = 0; i < NRB; ++i) load(p, xr, r0 + i, d[i]);
+#pragma unroll
+            for (int i = 0; i < NRB; ++i)
+                if (r0 + i < rounds) store(p, lds, r0 + i, d[i]);
+        }
+    }
+};
 
 // --------------------------------------------------------- row reductions
 // Cross-lane exchange partner l ^ D for D in {1, 2, 4, 8}, within 16-lane rows.
@@ -348,66 +441,89 @@ __device__ __forceinline__ int reduce_index(int lane)
 // Units in flight per wavefront (weight loads issued ahead of use).
 constexpr int prefetch_depth(int R, int M) { return (R * M <= 2) ? 4 : (R * M <= 8 ? 2 : 1); }
 
-template <int BITS, int GS, int R, int M, bool XF32>
+template <int BITS, int GS, int R, int M, bool XF32, bool SBF>
 __global__ __launch_bounds__(kMaxWaves * kWave) void qmv_affine_kernel(const Params p)
 {
     constexpr int LPG = GS * BITS / 128;          // lanes (chunks) per group
     constexpr int VPC = 128 / BITS;               // values per chunk
     constexpr int XCB = VPC * (XF32 ? 4 : 2);     // activation bytes per chunk in LDS
     constexpr int OFFSET = 1 << BITS;             // code offset of the bf16 pairs
-    constexpr int PF = prefetch_depth(R, M);
+    constexpr int PF = prefetch_depth(R, M);      // units in flight
+    constexpr int NS = PF + 1;                    // ring slots
     constexpr int V = R * M;
     constexpr int P = pow2_at_least(V);
     static_assert(P <= 64, "R*M must not exceed 64");
 
     extern __shared__ __align__(16) uint8_t lds[];
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
+    // wave-uniform by construction; readfirstlane lets the compiler keep it
+    // (and every buffer descriptor built from it) in scalar registers
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
     const int W = blockDim.x / kWave;
     const float* Slds = reinterpret_cast<const float*>(lds + p.s_off);
-    const int words_per_row = p.chunks * 4;
+    const int row_bytes = p.chunks * 16;
 
     if ((int)blockIdx.x >= p.n_rb) return;
     const int n_my = (p.n_rb - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
     const int n_units = n_my * p.nsteps;
+    const __amdgpu_buffer_rsrc_t xr =
+        make_rsrc(p.x, (long long)M * p.K * (XF32 ? 4 : 2));
 
-    // unit u of this wavefront: row block blockIdx.x + (u / nsteps) * gridDim.x, step u % nsteps
-    auto issue = [&](int u, uint4 (&wv)[R], uint32_t (&sv)[R], uint32_t (&bv)[R]) {
-        const int rbi = u / p.nsteps;
-        const int t = u - rbi * p.nsteps;
-        const int row0 = (((int)blockIdx.x + rbi * (int)gridDim.x) * W + wave) * R;
-        const int c = t * kWave + lane;
+    // Units are issued in order: unit (irb, it) is row block
+    // blockIdx.x + irb * gridDim.x, wave step it.  Buffer resources start at the
+    // wavefront's first row, so rows past N fall outside the record count and
+    // read as zero.  Every call issues the same 3R loads; units past the last
+    // one (irb >= n_my) get empty resources and read nothing.
+    int it = 0, irb = 0;
+    auto issue = [&](uint4 (&wv)[R], uint16_t (&sv)[R], uint16_t (&bv)[R]) {
+        const int row0 = (((int)blockIdx.x + irb * (int)gridDim.x) * W + wave) * R;
+        const long long rows_left = (irb < n_my) ? (long long)p.N - row0 : 0;
+        const __amdgpu_buffer_rsrc_t wr =
+            make_rsrc(reinterpret_cast<const uint8_t*>(p.w) + (size_t)row0 * row_bytes, rows_left * row_bytes);
+        const __amdgpu_buffer_rsrc_t sr = make_rsrc(p.s + (size_t)row0 * p.G, rows_left * p.G * 2);
+        const __amdgpu_buffer_rsrc_t br = make_rsrc(p.b + (size_t)row0 * p.G, rows_left * p.G * 2);
+        const int c = it * kWave + lane;
         const bool active = c < p.chunks;
-        const int grp = c / LPG;
+        const uint32_t wo = (uint32_t)opaque(active ? c * 16 : kOut);
+        const uint32_t mo = (uint32_t)opaque(active ? (c / LPG) * 2 : kOut);
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const bool ok = active && (row0 + r < p.N);
-            const size_t row = (size_t)(row0 + r);
-            wv[r] = ok ? load_nt(reinterpret_cast<const uint4*>(p.w + row * words_per_row) + c)
-                       : make_uint4(0, 0, 0, 0);
-            sv[r] = ok ? (uint32_t)p.s[row * p.G + grp] : 0u;
-            bv[r] = ok ? (uint32_t)p.b[row * p.G + grp] : 0u;
+            wv[r] = buf_load_nt(wr, (int)(wo + (uint32_t)(r * row_bytes)));
+            sv[r] = buf_load_u16(sr, (int)(mo + (uint32_t)(r * p.G * 2)));
+            bv[r] = buf_load_u16(br, (int)(mo + (uint32_t)(r * p.G * 2)));
+        }
+        if (++it == p.nsteps) {
+            it = 0;
+            ++irb;
         }
     };
 
-    uint4 wb[PF][R];
-    uint32_t sb[PF][R], bb[PF][R];
+    const uint32_t magic = code_magic<BITS>();
+    Stager<BITS, GS, M, XF32> stg;
+    uint4 wb[NS][R];
+    uint16_t sb[NS][R], bb[NS][R];
+    auto prologue = [&]() {
 #pragma unroll
-    for (int s = 0; s < PF; ++s)
-        if (s < n_units) issue(s, wb[s], sb[s], bb[s]);
-
+        for (int s = 0; s < PF; ++s) issue(wb[s], sb[s], bb[s]);
+    };
     if (p.nwin == 1) {
-        stage_x<BITS, GS, M, XF32>(p, lds, 0);
+        // stage the whole activation tile; the weight prefetch is issued right
+        // after the first batch of activation loads
+        stg.stage(p, xr, lds, 0, prologue);
         __syncthreads();
+    } else {
+        prologue();
     }
 
     float acc[R][M];
     int t = 0, rbi = 0;
-    for (int ub = 0; ub < n_units; ub += PF) {
+    for (int ub = 0; ub < n_units; ub += NS) {
 #pragma unroll
-        for (int s = 0; s < PF; ++s) {
+        for (int s = 0; s < NS; ++s) {
             const int u = ub + s;
             if (u < n_units) {
+                // the slot consumed one unit ago takes the unit PF ahead
+                issue(wb[(s + PF) % NS], sb[(s + PF) % NS], bb[(s + PF) % NS]);
                 if (t == 0) {
 #pragma unroll
                     for (int r = 0; r < R; ++r)
@@ -416,18 +532,16 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void qmv_affine_kernel(const Par
                 }
                 if (p.nwin > 1 && (t % p.win_steps) == 0) {
                     __syncthreads();
-                    stage_x<BITS, GS, M, XF32>(p, lds, t / p.win_steps);
+                    stg.stage(p, xr, lds, t / p.win_steps, [] {});
                     __syncthreads();
                 }
-                uint4 wcur[R];
+                const uint4 (&wcur)[R] = wb[s];
                 float sv[R], bv[R];
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
-                    wcur[r] = wb[s][r];
-                    sv[r] = p.sb_bf16 ? bf16_bits_to_f32(sb[s][r]) : f16_bits_to_f32(sb[s][r]);
-                    bv[r] = p.sb_bf16 ? bf16_bits_to_f32(bb[s][r]) : f16_bits_to_f32(bb[s][r]);
+                    sv[r] = SBF ? bf16_bits_to_f32((uint32_t)sb[s][r]) : f16_bits_to_f32((uint32_t)sb[s][r]);
+                    bv[r] = SBF ? bf16_bits_to_f32((uint32_t)bb[s][r]) : f16_bits_to_f32((uint32_t)bb[s][r]);
                 }
-                if (u + PF < n_units) issue(u + PF, wb[s], sb[s], bb[s]);
 
                 const int win = t / p.win_steps;
                 const int t_lo = win * p.win_steps;
@@ -443,7 +557,42 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void qmv_affine_kernel(const Par
                     constexpr int PPW = 16 / BITS;             // pairs per word
                     constexpr int NH = (BITS == 4) ? 1 : 2;    // decode passes per chunk
                     constexpr int WPH = 4 / NH;                // words per pass
-                    if constexpr (NH == 1) {
+                    if constexpr (NH == 1 && M <= R) {
+                        // few vectors: activation pairs of all M vectors first, then one
+                        // row at a time (decode, then every vector's chain and fold)
+                        uint32_t xp[M][4 * PPW];
+                        float S[M];
+#pragma unroll
+                        for (int m = 0; m < M; ++m) {
+                            const uint8_t* xs = lds + m * p.x_m_bytes;
+                            S[m] = Slds[m * p.gw + gl];
+#pragma unroll
+                            for (int v = 0; v < PPW; ++v) {
+                                const uint4 t4 = *reinterpret_cast<const uint4*>(xs + lds_phys(cl * XCB + v * 16));
+                                xp[m][4 * v + 0] = t4.x; xp[m][4 * v + 1] = t4.y;
+                                xp[m][4 * v + 2] = t4.z; xp[m][4 * v + 3] = t4.w;
+                            }
+                        }
+#pragma unroll
+                        for (int r = 0; r < R; ++r) {
+                            const uint32_t wd[4] = {wcur[r].x, wcur[r].y, wcur[r].z, wcur[r].w};
+                            uint32_t qp[4 * PPW];
+#pragma unroll
+                            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                                for (int j = 0; j < PPW; ++j) qp[i * PPW + j] = code_pair<BITS>(wd[i], j, magic);
+#pragma unroll
+                            for (int m = 0; m < M; ++m) {
+                                float d = 0.0f;
+#pragma unroll
+                                for (int i = 0; i < 4 * PPW; ++i) d = dot2(qp[i], xp[m][i], d);
+                                d = lane_group_sum<LPG>(d);
+                                d = __builtin_fmaf(-(float)OFFSET, S[m], d);
+                                const float na = __builtin_fmaf(sv[r], d, __builtin_fmaf(bv[r], S[m], acc[r][m]));
+                                acc[r][m] = owner ? na : acc[r][m];
+                            }
+                        }
+                    } else if constexpr (NH == 1) {
                         uint32_t qp[R][4 * PPW];
 #pragma unroll
                         for (int r = 0; r < R; ++r) {
@@ -451,7 +600,7 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void qmv_affine_kernel(const Par
 #pragma unroll
                             for (int i = 0; i < 4; ++i)
 #pragma unroll
-                                for (int j = 0; j < PPW; ++j) qp[r][i * PPW + j] = code_pair<BITS>(wd[i], j);
+                                for (int j = 0; j < PPW; ++j) qp[r][i * PPW + j] = code_pair<BITS>(wd[i], j, magic);
                         }
 #pragma unroll
                         for (int m = 0; m < M; ++m) {
@@ -487,7 +636,7 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void qmv_affine_kernel(const Par
                                 for (int i = 0; i < WPH; ++i)
 #pragma unroll
                                     for (int j = 0; j < PPW; ++j)
-                                        qp[r][i * PPW + j] = code_pair<BITS>(wd[h * WPH + i], j);
+                                        qp[r][i * PPW + j] = code_pair<BITS>(wd[h * WPH + i], j, magic);
                             }
 #pragma unroll
                             for (int m = 0; m < M; ++m) {
