@@ -18,7 +18,6 @@ namespace {
 using qmv::KernelFn;
 using qmv::Params;
 
-constexpr int kWavesPerWg = 8;
 
 int dtype_bytes(int dt) { return dt == QMV_DT_F32 ? 4 : 2; }
 
@@ -69,30 +68,20 @@ KernelFn pick_kernel(int bits, int gs, bool xf32, bool sbf, int R, int M)
     return xf32 ? qmv::qmv_table_b2_g128_f32[ri][mi][si] : qmv::qmv_table_b2_g128_bf16[ri][mi][si];
 }
 
-// Library choice of rows per wavefront.
-int default_rows(int M, int G, bool xf32)
-{
-    (void)G;
-    int R = (M <= 2) ? 2 : 4;
-    if (xf32 && M > 4) R = 2;
-    return R;
-}
-
 struct Plan {
     Params p;
     KernelFn fn;
-    int R, W, lds, grid_cap_rb;
+    int R, W, lds, grid, blocks_per_cu;
 };
 
 // LDS layout and K windows.  Returns QMV_E_SHAPE if one wave step of
 // activations for all M vectors does not fit in LDS.
-int make_plan(int M, int N, int K, int bits, int gs, bool xf32, bool sbf, int R, Plan& pl)
+int make_plan(int M, int N, int K, int bits, int gs, bool xf32, bool sbf, int R, int W, Plan& pl)
 {
     const int G = K / gs;
     const int lpg = gs * bits / 128;
     const int chunks = K * bits / 128;
     const int nsteps = (chunks + qmv::kWave - 1) / qmv::kWave;
-    const int W = kWavesPerWg;
     const int xcb = (128 / bits) * (xf32 ? 4 : 2);
     int ws = nsteps, x_m = 0, s_bytes = 0, total = 0;
     for (;;) {
@@ -132,12 +121,15 @@ int make_plan(int M, int N, int K, int bits, int gs, bool xf32, bool sbf, int R,
 
 // Per-device launch-shape cache: compute-unit count, and for each kernel
 // instance and LDS size the resident workgroups per CU (after raising the
-// instance's dynamic-LDS limit).  Filled on first use; never invalidated.
+// instance's dynamic-LDS limit) and the instance's private (spill) bytes per
+// lane.  Filled on first use; never invalidated.
 struct OccEntry {
     const void* fn;
     int dev;
     int lds;
+    int w;
     int blocks;
+    int scratch;
 };
 
 std::mutex g_mu;
@@ -157,47 +149,113 @@ int cu_count_locked(int dev)
     return g_cus[dev];
 }
 
-// Workgroups: as many as stay resident (occupancy x CUs), at most one per row
-// block, balanced so every workgroup walks the same number of row blocks.
-// Returns -1 on a HIP error.
-int plan_grid(Plan& pl, int* blocks_per_cu)
+// Resident workgroups per CU of an instance at a workgroup size and LDS size,
+// and its private bytes per lane (cached; raises the instance's dynamic-LDS
+// limit on first use).  False on a HIP error.
+bool occupancy(KernelFn kfn, int W, int lds, int dev, int& blocks, int& scratch)
+{
+    const void* fn = reinterpret_cast<const void*>(kfn);
+    std::lock_guard<std::mutex> lk(g_mu);
+    for (int i = 0; i < g_nocc; ++i)
+        if (g_occ[i].fn == fn && g_occ[i].dev == dev && g_occ[i].lds == lds && g_occ[i].w == W) {
+            blocks = g_occ[i].blocks;
+            scratch = g_occ[i].scratch;
+            return true;
+        }
+    if (lds > 65536 && hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
+        return false;
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, W * qmv::kWave, lds) != hipSuccess) return false;
+    hipFuncAttributes attr;
+    if (hipFuncGetAttributes(&attr, fn) != hipSuccess) return false;
+    blocks = nb < 0 ? 0 : nb;
+    scratch = (int)attr.localSizeBytes;
+    if (g_nocc < 1024) g_occ[g_nocc++] = OccEntry{fn, dev, lds, W, blocks, scratch};
+    return true;
+}
+
+int cu_count(int dev)
+{
+    std::lock_guard<std::mutex> lk(g_mu);
+    return cu_count_locked(dev);
+}
+
+// Relative VALU issue efficiency at a number of resident wavefronts per SIMD
+// (measured on gfx950 with independent fma chains: one wavefront per SIMD
+// reaches about a third of the rate, four about 90%).
+double wave_efficiency(double wps)
+{
+    if (wps >= 8) return 1.0;
+    if (wps >= 4) return 0.87 + (wps - 4) * 0.13 / 4;
+    if (wps >= 2) return 0.60 + (wps - 2) * 0.27 / 2;
+    if (wps >= 1) return 0.31 + (wps - 1) * 0.29;
+    return 0.31 * wps;
+}
+
+// Launch shape: rows per wavefront R (given, or searched over 4, 2, 1) and
+// wavefronts per workgroup W, chosen to minimise the rows the busiest CU
+// must stream divided by the issue efficiency of its resident wavefronts.
+// The grid holds every resident workgroup (at most one per row block), and
+// each workgroup walks an equal share of the row blocks.  Instances that
+// spill registers are used only when no other instance fits.  2-bit codes
+// have no four-row instances; a request for four rows gets two.
+int choose_plan(int M, int N, int K, int bits, int gs, bool xf32, bool sbf, int R_req, Plan& best)
 {
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return -1;
-    const void* fn = reinterpret_cast<const void*>(pl.fn);
-    std::lock_guard<std::mutex> lk(g_mu);
-    int nb = -1;
-    for (int i = 0; i < g_nocc; ++i)
-        if (g_occ[i].fn == fn && g_occ[i].dev == dev && g_occ[i].lds == pl.lds) {
-            nb = g_occ[i].blocks;
-            break;
+    if (hipGetDevice(&dev) != hipSuccess) return QMV_E_LAUNCH;
+    const int cus = cu_count(dev);
+    if (bits == 2 && R_req == 4) R_req = 2;
+    const int Rs[3] = {4, 2, 1};
+    double best_score = 0.0;
+    bool found = false, best_spills = false, shape_ok = false;
+    for (int ri = 0; ri < 3; ++ri) {
+        const int R = Rs[ri];
+        if (R_req != 0 && R != R_req) continue;
+        const int maxW = qmv::max_waves(bits, xf32, R, M);
+        for (int W = maxW; W >= 1; --W) {
+            Plan pl;
+            if (make_plan(M, N, K, bits, gs, xf32, sbf, R, W, pl) != QMV_OK) continue;
+            shape_ok = true;
+            if (pl.fn == nullptr) continue;
+            int nb = 0, scratch = 0;
+            if (!occupancy(pl.fn, W, pl.lds, dev, nb, scratch)) return QMV_E_LAUNCH;
+            if (nb == 0) continue;
+            const bool spills = scratch > 0;
+            const int n_rb = pl.p.n_rb;
+            const int cap = nb * cus;
+            const int per = (n_rb + cap - 1) / cap;          // row blocks per workgroup
+            const int grid = (n_rb + per - 1) / per;
+            const int wg_cu = (grid + cus - 1) / cus;        // workgroups on the busiest CU
+            const double rows_cu = (double)wg_cu * per * W * R;
+            const double wps = (double)std::min(nb, wg_cu) * W / 4.0;
+            double score = rows_cu / wave_efficiency(wps);
+            if (R == 1) score *= 1.25;      // x reads from LDS are not shared across rows
+            else if (R == 2) score *= 1.04;
+            const bool better = !found || (best_spills && !spills) ||
+                                (best_spills == spills && score < best_score - 1e-9);
+            if (better) {
+                found = true;
+                best_spills = spills;
+                best_score = score;
+                best = pl;
+                best.grid = grid;
+                best.blocks_per_cu = nb;
+            }
         }
-    if (nb < 0) {
-        if (pl.lds > 65536 &&
-            hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, pl.lds) != hipSuccess)
-            return -1;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, pl.W * qmv::kWave, pl.lds) != hipSuccess)
-            return -1;
-        if (nb < 1) nb = 1;
-        if (g_nocc < 1024) g_occ[g_nocc++] = OccEntry{fn, dev, pl.lds, nb};
     }
-    if (blocks_per_cu) *blocks_per_cu = nb;
-    const int cap = nb * cu_count_locked(dev);
-    const int n_rb = pl.p.n_rb;
-    const int per = (n_rb + cap - 1) / cap;
-    return (n_rb + per - 1) / per;
+    if (!found) return shape_ok ? QMV_E_LAUNCH : QMV_E_SHAPE;
+    return QMV_OK;
 }
 
 // Vectors per launch: all M, unless one wave step of activations for M
 // vectors does not fit in LDS (fp32 activations with 2-bit codes); then the
 // largest count that fits.  Vectors are independent, so splitting M changes
 // no result bit.
-int vectors_per_launch(int M, int N, int K, int bits, int gs, bool xf32, int R_req)
+int vectors_per_launch(int M, int N, int K, int bits, int gs, bool xf32)
 {
     for (int mc = M; mc >= 1; --mc) {
         Plan pl;
-        const int R = R_req ? R_req : default_rows(mc, K / gs, xf32);
-        if (make_plan(mc, N, K, bits, gs, xf32, true, R, pl) == QMV_OK) return mc;
+        if (make_plan(mc, N, K, bits, gs, xf32, true, 1, 1, pl) == QMV_OK) return mc;
     }
     return 0;
 }
@@ -215,14 +273,13 @@ int qmv_affine_ex(const uint32_t* w_packed, const void* scales, const void* bias
                         y_dt, rows_per_wave);
     if (st != QMV_OK) return st;
     const bool xf32 = (x_dt == QMV_DT_F32);
-    const int G = K / group_size;
-    const int mc = vectors_per_launch(M, N, K, bits, group_size, xf32, rows_per_wave);
+    const bool sbf = (sb_dt == QMV_DT_BF16);
+    const int mc = vectors_per_launch(M, N, K, bits, group_size, xf32);
     if (mc < 1) return QMV_E_SHAPE;
     for (int m0 = 0; m0 < M; m0 += mc) {
         const int mm = std::min(mc, M - m0);
-        const int R = rows_per_wave ? rows_per_wave : default_rows(mm, G, xf32);
         Plan pl;
-        st = make_plan(mm, N, K, bits, group_size, xf32, sb_dt == QMV_DT_BF16, R, pl);
+        st = choose_plan(mm, N, K, bits, group_size, xf32, sbf, rows_per_wave, pl);
         if (st != QMV_OK) return st;
         Params& p = pl.p;
         p.w = w_packed;
@@ -231,10 +288,8 @@ int qmv_affine_ex(const uint32_t* w_packed, const void* scales, const void* bias
         p.x = static_cast<const uint8_t*>(x) + (size_t)m0 * K * dtype_bytes(x_dt);
         p.y = static_cast<uint8_t*>(y) + (size_t)m0 * N * dtype_bytes(y_dt);
         p.y_bf16 = (y_dt == QMV_DT_BF16);
-        const int grid = plan_grid(pl, nullptr);
-        if (grid < 1) return QMV_E_LAUNCH;
         void* args[] = {&p};
-        const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(pl.fn), dim3(grid),
+        const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(pl.fn), dim3(pl.grid),
                                              dim3(pl.W * qmv::kWave), args, (size_t)pl.lds,
                                              static_cast<hipStream_t>(stream));
         if (e != hipSuccess) return QMV_E_LAUNCH;
@@ -262,24 +317,20 @@ int qmv_kernel_info(int M, int N, int K, int bits, int group_size, qmv_dtype x_d
                         QMV_DT_BF16, QMV_DT_F32, rows_per_wave);
     if (st != QMV_OK) return st;
     const bool xf32 = (x_dt == QMV_DT_F32);
-    const int mc = vectors_per_launch(M, N, K, bits, group_size, xf32, rows_per_wave);
+    const int mc = vectors_per_launch(M, N, K, bits, group_size, xf32);
     if (mc < 1) return QMV_E_SHAPE;
-    const int R = rows_per_wave ? rows_per_wave : default_rows(mc, K / group_size, xf32);
     Plan pl;
-    st = make_plan(mc, N, K, bits, group_size, xf32, true, R, pl);
+    st = choose_plan(mc, N, K, bits, group_size, xf32, true, rows_per_wave, pl);
     if (st != QMV_OK) return st;
-    int nb = 0;
-    const int grid = plan_grid(pl, &nb);
-    if (grid < 1) return QMV_E_LAUNCH;
     hipFuncAttributes attr;
     if (hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(pl.fn)) != hipSuccess) return QMV_E_LAUNCH;
     out->vgprs = attr.numRegs;
     out->scratch_bytes = (int)attr.localSizeBytes;
     out->lds_bytes = pl.lds;
     out->wg_size = pl.W * qmv::kWave;
-    out->grid = grid;
-    out->waves_per_simd = nb * pl.W / 4;
-    out->rows_per_wave = R;
+    out->grid = pl.grid;
+    out->waves_per_simd = std::min(pl.blocks_per_cu, (pl.grid + 255) / 256) * pl.W / 4;
+    out->rows_per_wave = pl.R;
     out->k_windows = pl.p.nwin;
     return QMV_OK;
 }

@@ -40,8 +40,10 @@
 //      D = D' (fp32 path).  S[m][g] is the fp32 sum of the group's activations:
 //      8-value blocks summed left to right, blocks combined pairwise
 //      (xor-1, xor-2, ... tree).
-//   4. The group's owner lane (lane % lpg == step % lpg) folds once per group:
+//   4. Each group is folded once, by its owner lane (lane % lpg == step % lpg):
 //      acc = fma(scale, D, fma(bias, S, acc)), over its groups in ascending step.
+//      Every lane executes the fold; scale and bias read as zero on the other
+//      lanes, whose accumulators it leaves unchanged (up to the sign of a zero).
 //   5. Row total: lanes l and l ^ d combined for d = 32, 16, 8, 4, 2, 1 in that
 //      order; then round-to-nearest-even to y's dtype.
 #pragma once
@@ -55,7 +57,6 @@
 namespace qmv {
 
 constexpr int kWave = 64;
-constexpr int kMaxWaves = 8;
 constexpr int kLdsBytes = 163840;
 
 struct Params {
@@ -196,9 +197,39 @@ __device__ __forceinline__ int opaque(int v)
     return v;
 }
 
+// Returns v unchanged from an empty volatile asm: the computation of v stays
+// where it is written (it cannot be sunk into later blocks, which would keep
+// its inputs live).
+__device__ __forceinline__ float pinned(float v)
+{
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
+// Returns v unchanged, as a value that exists only once `dep` has been
+// computed: a memory access addressed by it cannot be moved (by IR passes or
+// the scheduler) above the computation of `dep`.
+__device__ __forceinline__ int after(int v, float dep)
+{
+    asm volatile("" : "+v"(v) : "v"(dep));
+    return v;
+}
+
 __device__ __forceinline__ uint16_t buf_load_u16(__amdgpu_buffer_rsrc_t r, int off)
 {
     return (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+
+// Two 16-bit loads into the halves of one register (lo from ra, hi from rb):
+// the compiler emits a d16 load and a d16_hi load into the same VGPR.
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t buf_load_u16_pair(__amdgpu_buffer_rsrc_t ra, int oa,
+                                                      __amdgpu_buffer_rsrc_t rb, int ob)
+{
+    u16x2 v;
+    v.x = (unsigned short)__builtin_amdgcn_raw_buffer_load_b16(ra, oa, 0, 0);
+    v.y = (unsigned short)__builtin_amdgcn_raw_buffer_load_b16(rb, ob, 0, 0);
+    return __builtin_bit_cast(uint32_t, v);
 }
 
 // ------------------------------------------------------ activation staging
@@ -321,8 +352,10 @@ struct Stager {
     }
 
     // Stage a window: the loads of up to NRB rounds are issued together, then
-    // stored.  `between` runs after the first batch's loads are issued (the
-    // caller issues its weight prefetch there, so both streams overlap).
+    // stored.  `between` runs after the first batch's loads are issued by every
+    // wavefront of the workgroup (a barrier orders them): the caller issues its
+    // weight prefetch there, so the activation requests sit ahead of the
+    // weight stream in the compute unit's queue and both overlap.
     template <class F>
     __device__ void stage(const Params& p, __amdgpu_buffer_rsrc_t xr, uint8_t* lds, int win, F&& between)
     {
@@ -331,6 +364,7 @@ struct Stager {
             uint4 d[NRB][NLD];
 #pragma unroll
             for (int i = 0; i < NRB; ++i) load(p, xr, i, d[i]);
+            __syncthreads();
             between();
 #pragma unroll
             for (int i = 0; i < NRB; ++i)
@@ -441,8 +475,16 @@ __device__ __forceinline__ int reduce_index(int lane)
 // Units in flight per wavefront (weight loads issued ahead of use).
 constexpr int prefetch_depth(int R, int M) { return (R * M <= 2) ? 4 : (R * M <= 8 ? 2 : 1); }
 
+// Largest workgroup (in wavefronts) an instance is compiled for: 16 when its
+// registers fit four wavefronts per SIMD (4-bit codes, bf16 activations, few
+// rows x vectors), else 8.
+constexpr int max_waves(int BITS, bool XF32, int R, int M)
+{
+    return (BITS == 4 && !XF32 && R * M <= 4) ? 16 : 8;
+}
+
 template <int BITS, int GS, int R, int M, bool XF32, bool SBF>
-__global__ __launch_bounds__(kMaxWaves * kWave) void qmv_affine_kernel(const Params p)
+__global__ __launch_bounds__(max_waves(BITS, XF32, R, M) * kWave) void qmv_affine_kernel(const Params p)
 {
     constexpr int LPG = GS * BITS / 128;          // lanes (chunks) per group
     constexpr int VPC = 128 / BITS;               // values per chunk
@@ -475,7 +517,7 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void qmv_affine_kernel(const Par
     // read as zero.  Every call issues the same 3R loads; units past the last
     // one (irb >= n_my) get empty resources and read nothing.
     int it = 0, irb = 0;
-    auto issue = [&](uint4 (&wv)[R], uint16_t (&sv)[R], uint16_t (&bv)[R]) {
+    auto issue = [&](uint4 (&wv)[R], uint32_t (&sbv)[R]) {
         const int row0 = (((int)blockIdx.x + irb * (int)gridDim.x) * W + wave) * R;
         const long long rows_left = (irb < n_my) ? (long long)p.N - row0 : 0;
         const __amdgpu_buffer_rsrc_t wr =
@@ -484,13 +526,16 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void qmv_affine_kernel(const Par
         const __amdgpu_buffer_rsrc_t br = make_rsrc(p.b + (size_t)row0 * p.G, rows_left * p.G * 2);
         const int c = it * kWave + lane;
         const bool active = c < p.chunks;
+        // scale and bias are read by the group's owner lane only; on every other
+        // lane they read as zero, which turns its fold into a no-op
+        const bool own = active && ((lane % LPG) == (it % LPG));
         const uint32_t wo = (uint32_t)opaque(active ? c * 16 : kOut);
-        const uint32_t mo = (uint32_t)opaque(active ? (c / LPG) * 2 : kOut);
+        const uint32_t mo = (uint32_t)opaque(own ? (c / LPG) * 2 : kOut);
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             wv[r] = buf_load_nt(wr, (int)(wo + (uint32_t)(r * row_bytes)));
-            sv[r] = buf_load_u16(sr, (int)(mo + (uint32_t)(r * p.G * 2)));
-            bv[r] = buf_load_u16(br, (int)(mo + (uint32_t)(r * p.G * 2)));
+            const int o = (int)(mo + (uint32_t)(r * p.G * 2));
+            sbv[r] = buf_load_u16_pair(sr, o, br, o);
         }
         if (++it == p.nsteps) {
             it = 0;
@@ -501,10 +546,10 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void qmv_affine_kernel(const Par
     const uint32_t magic = code_magic<BITS>();
     Stager<BITS, GS, M, XF32> stg;
     uint4 wb[NS][R];
-    uint16_t sb[NS][R], bb[NS][R];
+    uint32_t sbb[NS][R];    // scale (low half) and bias (high half) bits
     auto prologue = [&]() {
 #pragma unroll
-        for (int s = 0; s < PF; ++s) issue(wb[s], sb[s], bb[s]);
+        for (int s = 0; s < PF; ++s) issue(wb[s], sbb[s]);
     };
     if (p.nwin == 1) {
         // stage the whole activation tile; the weight prefetch is issued right
@@ -523,7 +568,7 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void qmv_affine_kernel(const Par
             const int u = ub + s;
             if (u < n_units) {
                 // the slot consumed one unit ago takes the unit PF ahead
-                issue(wb[(s + PF) % NS], sb[(s + PF) % NS], bb[(s + PF) % NS]);
+                issue(wb[(s + PF) % NS], sbb[(s + PF) % NS]);
                 if (t == 0) {
 #pragma unroll
                     for (int r = 0; r < R; ++r)
@@ -536,11 +581,15 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void qmv_affine_kernel(const Par
                     __syncthreads();
                 }
                 const uint4 (&wcur)[R] = wb[s];
+                // Scale and bias of each row's group: zero on every lane but the
+                // group's owner, so the fold acc = s*D + (b*S + acc) leaves a
+                // non-owner's accumulator unchanged without a branch.
                 float sv[R], bv[R];
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
-                    sv[r] = SBF ? bf16_bits_to_f32((uint32_t)sb[s][r]) : f16_bits_to_f32((uint32_t)sb[s][r]);
-                    bv[r] = SBF ? bf16_bits_to_f32((uint32_t)bb[s][r]) : f16_bits_to_f32((uint32_t)bb[s][r]);
+                    const uint32_t v = sbb[s][r];
+                    sv[r] = SBF ? __uint_as_float(v << 16) : f16_bits_to_f32(v & 0xffffu);
+                    bv[r] = SBF ? __uint_as_float(v & 0xffff0000u) : f16_bits_to_f32(v >> 16);
                 }
 
                 const int win = t / p.win_steps;
@@ -549,131 +598,105 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void qmv_affine_kernel(const Par
                 const bool active = c < p.chunks;
                 const int grp = active ? c / LPG : 0;        // group of the chunk
                 const int gl = active ? grp - win * p.gw : 0;  // group within the window
-                const bool owner = active && ((lane % LPG) == (t % LPG));
-                const int cl = c - t_lo * kWave;             // chunk within the window
+                // chunk within the window; a lane past the last chunk reads the
+                // window's first chunk (staged, finite values; its weights read as
+                // zero and its scale and bias too, so its fold adds nothing)
+                const int cl = active ? c - t_lo * kWave : 0;
 
                 if constexpr (!XF32) {
                     // ---- bf16 activations: exact code pairs and v_dot2_f32_bf16
+                    constexpr int NP = 64 / BITS;              // code pairs per chunk
                     constexpr int PPW = 16 / BITS;             // pairs per word
-                    constexpr int NH = (BITS == 4) ? 1 : 2;    // decode passes per chunk
-                    constexpr int WPH = 4 / NH;                // words per pass
-                    if constexpr (NH == 1 && M <= R) {
+                    // activation pairs of vector m for this lane's chunk, and the group's
+                    // sum.  xo is the chunk's LDS offset lds_phys(cl * XCB), possibly tied
+                    // to an earlier result by after(); a chunk never straddles a padding
+                    // point, so its 16-byte pieces sit at xo + 16 v.
+                    const int xo0 = lds_phys(cl * XCB);
+                    auto read_x = [&](int m, int xo, uint32_t (&xp)[NP], float& S) {
+                        const uint8_t* xs = lds + m * p.x_m_bytes + xo;
+                        S = Slds[m * p.gw + gl];
+#pragma unroll
+                        for (int v = 0; v < NP / 4; ++v) {
+                            const uint4 t4 = *reinterpret_cast<const uint4*>(xs + v * 16);
+                            xp[4 * v + 0] = t4.x; xp[4 * v + 1] = t4.y;
+                            xp[4 * v + 2] = t4.z; xp[4 * v + 3] = t4.w;
+                        }
+                    };
+                    auto decode = [&](const uint4& w4, uint32_t (&qp)[NP]) {
+                        const uint32_t wd[4] = {w4.x, w4.y, w4.z, w4.w};
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+#pragma unroll
+                            for (int j = 0; j < PPW; ++j) qp[i * PPW + j] = code_pair<BITS>(wd[i], j, magic);
+                    };
+                    // one vector's chain over a row's pairs, the offset removed, and the
+                    // fold of the group (a no-op on all lanes but the owner)
+                    auto chain_fold = [&](const uint32_t (&qp)[NP], const uint32_t (&xp)[NP], float S,
+                                          int r, float& a) {
+                        float d = 0.0f;
+#pragma unroll
+                        for (int i = 0; i < NP; ++i) d = dot2(qp[i], xp[i], d);
+                        d = lane_group_sum<LPG>(d);
+                        d = __builtin_fmaf(-(float)OFFSET, S, d);
+                        a = pinned(__builtin_fmaf(sv[r], d, __builtin_fmaf(bv[r], S, a)));
+                    };
+                    if constexpr (M <= R) {
                         // few vectors: activation pairs of all M vectors first, then one
                         // row at a time (decode, then every vector's chain and fold)
-                        uint32_t xp[M][4 * PPW];
+                        uint32_t xp[M][NP];
                         float S[M];
 #pragma unroll
-                        for (int m = 0; m < M; ++m) {
-                            const uint8_t* xs = lds + m * p.x_m_bytes;
-                            S[m] = Slds[m * p.gw + gl];
-#pragma unroll
-                            for (int v = 0; v < PPW; ++v) {
-                                const uint4 t4 = *reinterpret_cast<const uint4*>(xs + lds_phys(cl * XCB + v * 16));
-                                xp[m][4 * v + 0] = t4.x; xp[m][4 * v + 1] = t4.y;
-                                xp[m][4 * v + 2] = t4.z; xp[m][4 * v + 3] = t4.w;
-                            }
-                        }
+                        for (int m = 0; m < M; ++m) read_x(m, xo0, xp[m], S[m]);
 #pragma unroll
                         for (int r = 0; r < R; ++r) {
-                            const uint32_t wd[4] = {wcur[r].x, wcur[r].y, wcur[r].z, wcur[r].w};
-                            uint32_t qp[4 * PPW];
+                            uint32_t qp[NP];
+                            decode(wcur[r], qp);
 #pragma unroll
-                            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                                for (int j = 0; j < PPW; ++j) qp[i * PPW + j] = code_pair<BITS>(wd[i], j, magic);
-#pragma unroll
-                            for (int m = 0; m < M; ++m) {
-                                float d = 0.0f;
-#pragma unroll
-                                for (int i = 0; i < 4 * PPW; ++i) d = dot2(qp[i], xp[m][i], d);
-                                d = lane_group_sum<LPG>(d);
-                                d = __builtin_fmaf(-(float)OFFSET, S[m], d);
-                                const float na = __builtin_fmaf(sv[r], d, __builtin_fmaf(bv[r], S[m], acc[r][m]));
-                                acc[r][m] = owner ? na : acc[r][m];
-                            }
-                        }
-                    } else if constexpr (NH == 1) {
-                        uint32_t qp[R][4 * PPW];
-#pragma unroll
-                        for (int r = 0; r < R; ++r) {
-                            const uint32_t wd[4] = {wcur[r].x, wcur[r].y, wcur[r].z, wcur[r].w};
-#pragma unroll
-                            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                                for (int j = 0; j < PPW; ++j) qp[r][i * PPW + j] = code_pair<BITS>(wd[i], j, magic);
-                        }
-#pragma unroll
-                        for (int m = 0; m < M; ++m) {
-                            const uint8_t* xs = lds + m * p.x_m_bytes;
-                            const float S = Slds[m * p.gw + gl];
-                            uint32_t xp[4 * PPW];
-#pragma unroll
-                            for (int v = 0; v < PPW; ++v) {
-                                const uint4 t4 = *reinterpret_cast<const uint4*>(xs + lds_phys(cl * XCB + v * 16));
-                                xp[4 * v + 0] = t4.x; xp[4 * v + 1] = t4.y;
-                                xp[4 * v + 2] = t4.z; xp[4 * v + 3] = t4.w;
-                            }
-#pragma unroll
-                            for (int r = 0; r < R; ++r) {
-                                float d = 0.0f;
-#pragma unroll
-                                for (int i = 0; i < 4 * PPW; ++i) d = dot2(qp[r][i], xp[i], d);
-                                d = lane_group_sum<LPG>(d);
-                                d = __builtin_fmaf(-(float)OFFSET, S, d);
-                                const float na = __builtin_fmaf(sv[r], d, __builtin_fmaf(bv[r], S, acc[r][m]));
-                                acc[r][m] = owner ? na : acc[r][m];
-                            }
+                            for (int m = 0; m < M; ++m) chain_fold(qp, xp[m], S[m], r, acc[r][m]);
                         }
                     } else {
-                        float dsum[R][M];
+                        // many vectors: decode every row once, then one vector at a time.
+                        // Vector m+1's pairs are read while vector m's chains run; the
+                        // read is tied to vector m-1's last result, so the compiler
+                        // cannot hoist every vector's reads (and registers) up front.
+                        uint32_t xq[2][NP];
+                        float Sq[2];
+                        read_x(0, xo0, xq[0], Sq[0]);
+                        uint32_t qp[R][NP];
 #pragma unroll
-                        for (int h = 0; h < NH; ++h) {
-                            uint32_t qp[R][WPH * PPW];
-#pragma unroll
-                            for (int r = 0; r < R; ++r) {
-                                const uint32_t wd[4] = {wcur[r].x, wcur[r].y, wcur[r].z, wcur[r].w};
-#pragma unroll
-                                for (int i = 0; i < WPH; ++i)
-#pragma unroll
-                                    for (int j = 0; j < PPW; ++j)
-                                        qp[r][i * PPW + j] = code_pair<BITS>(wd[h * WPH + i], j, magic);
-                            }
-#pragma unroll
-                            for (int m = 0; m < M; ++m) {
-                                const uint8_t* xs = lds + m * p.x_m_bytes;
-                                uint32_t xp[WPH * PPW];
-#pragma unroll
-                                for (int v = 0; v < WPH * PPW / 4; ++v) {
-                                    const uint4 t4 = *reinterpret_cast<const uint4*>(
-                                        xs + lds_phys(cl * XCB + h * (XCB / NH) + v * 16));
-                                    xp[4 * v + 0] = t4.x; xp[4 * v + 1] = t4.y;
-                                    xp[4 * v + 2] = t4.z; xp[4 * v + 3] = t4.w;
-                                }
-#pragma unroll
-                                for (int r = 0; r < R; ++r) {
-                                    float d = (h == 0) ? 0.0f : dsum[r][m];
-#pragma unroll
-                                    for (int i = 0; i < WPH * PPW; ++i) d = dot2(qp[r][i], xp[i], d);
-                                    dsum[r][m] = d;
-                                }
-                            }
-                        }
+                        for (int r = 0; r < R; ++r) decode(wcur[r], qp[r]);
 #pragma unroll
                         for (int m = 0; m < M; ++m) {
-                            const float S = Slds[m * p.gw + gl];
-#pragma unroll
-                            for (int r = 0; r < R; ++r) {
-                                float d = lane_group_sum<LPG>(dsum[r][m]);
-                                d = __builtin_fmaf(-(float)OFFSET, S, d);
-                                const float na = __builtin_fmaf(sv[r], d, __builtin_fmaf(bv[r], S, acc[r][m]));
-                                acc[r][m] = owner ? na : acc[r][m];
+                            if (m + 1 < M) {
+                                const int xo = (m == 0) ? xo0 : after(xo0, acc[R - 1][m - 1]);
+                                read_x(m + 1, xo, xq[(m + 1) & 1], Sq[(m + 1) & 1]);
                             }
+#pragma unroll
+                            for (int r = 0; r < R; ++r) chain_fold(qp[r], xq[m & 1], Sq[m & 1], r, acc[r][m]);
+                            // keep each vector's folds next to its chains (left free, the
+                            // scheduler sinks them and holds every chain result live)
+                            __builtin_amdgcn_sched_barrier(0);
                         }
                     }
                 } else {
-                    // ---- fp32 activations: exact fp32 codes and an fma chain
+                    // ---- fp32 activations: exact fp32 codes and an fma chain, one
+                    // weight word at a time; the activations of step k+1 (word, vector)
+                    // are read while step k's chains run
                     constexpr int VPW = 32 / BITS;             // values per word
                     float dsum[R][M];
+                    float xq[2][VPW];
+                    const int xo0 = lds_phys(cl * XCB);      // a chunk never straddles padding
+                    auto read_x = [&](int k, int xo, float (&xv)[VPW]) {
+                        const int i = k / M, m = k % M;
+                        const uint8_t* xs = lds + m * p.x_m_bytes + xo + i * VPW * 4;
+#pragma unroll
+                        for (int v = 0; v < VPW / 4; ++v) {
+                            const float4 t4 = *reinterpret_cast<const float4*>(xs + v * 16);
+                            xv[4 * v + 0] = t4.x; xv[4 * v + 1] = t4.y;
+                            xv[4 * v + 2] = t4.z; xv[4 * v + 3] = t4.w;
+                        }
+                    };
+                    read_x(0, xo0, xq[0]);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         float qv[R][VPW];
@@ -687,15 +710,13 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void qmv_affine_kernel(const Par
                         }
 #pragma unroll
                         for (int m = 0; m < M; ++m) {
-                            const uint8_t* xs = lds + m * p.x_m_bytes;
-                            float xv[VPW];
-#pragma unroll
-                            for (int v = 0; v < VPW / 4; ++v) {
-                                const float4 t4 = *reinterpret_cast<const float4*>(
-                                    xs + lds_phys(cl * XCB + i * VPW * 4 + v * 16));
-                                xv[4 * v + 0] = t4.x; xv[4 * v + 1] = t4.y;
-                                xv[4 * v + 2] = t4.z; xv[4 * v + 3] = t4.w;
+                            // step k+1's read is tied to step k-1's last chain result
+                            const int k = i * M + m;
+                            if (k + 1 < 4 * M) {
+                                const int xo = (k == 0) ? xo0 : after(xo0, dsum[R - 1][(k - 1) % M]);
+                                read_x(k + 1, xo, xq[(k + 1) & 1]);
                             }
+                            const float (&xv)[VPW] = xq[k & 1];
 #pragma unroll
                             for (int r = 0; r < R; ++r) {
                                 float d = (i == 0) ? 0.0f : dsum[r][m];
@@ -711,8 +732,7 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void qmv_affine_kernel(const Par
 #pragma unroll
                         for (int r = 0; r < R; ++r) {
                             const float d = lane_group_sum<LPG>(dsum[r][m]);
-                            const float na = __builtin_fmaf(sv[r], d, __builtin_fmaf(bv[r], S, acc[r][m]));
-                            acc[r][m] = owner ? na : acc[r][m];
+                            acc[r][m] = pinned(__builtin_fmaf(sv[r], d, __builtin_fmaf(bv[r], S, acc[r][m])));
                         }
                     }
                 }
