@@ -57,26 +57,36 @@ int check_args(const uint32_t* w, const void* s, const void* b, const void* x, v
     return QMV_OK;
 }
 
-KernelFn pick_kernel(int bits, int gs, bool xf32, bool sbf, int R, int M)
+int pf_index(int PF) { return PF == 1 ? 0 : (PF == 2 ? 1 : 2); }
+
+KernelFn pick_kernel(int bits, int gs, bool xf32, bool sbf, int R, int PF, int M, bool win)
 {
     const int ri = r_index(R);
+    const int pi = pf_index(PF);
     const int mi = M - 1;
     const int si = sbf ? 1 : 0;
-    if (bits == 4 && gs == 64) return xf32 ? qmv::qmv_table_b4_g64_f32[ri][mi][si] : qmv::qmv_table_b4_g64_bf16[ri][mi][si];
-    if (bits == 4 && gs == 128) return xf32 ? qmv::qmv_table_b4_g128_f32[ri][mi][si] : qmv::qmv_table_b4_g128_bf16[ri][mi][si];
-    if (bits == 2 && gs == 64) return xf32 ? qmv::qmv_table_b2_g64_f32[ri][mi][si] : qmv::qmv_table_b2_g64_bf16[ri][mi][si];
-    return xf32 ? qmv::qmv_table_b2_g128_f32[ri][mi][si] : qmv::qmv_table_b2_g128_bf16[ri][mi][si];
+    if (win) {
+        if (PF != 1) return nullptr;
+        if (bits == 4 && gs == 64) return xf32 ? qmv::qmv_wtable_b4_g64_f32[ri][mi][si] : qmv::qmv_wtable_b4_g64_bf16[ri][mi][si];
+        if (bits == 4 && gs == 128) return xf32 ? qmv::qmv_wtable_b4_g128_f32[ri][mi][si] : qmv::qmv_wtable_b4_g128_bf16[ri][mi][si];
+        if (bits == 2 && gs == 64) return xf32 ? qmv::qmv_wtable_b2_g64_f32[ri][mi][si] : qmv::qmv_wtable_b2_g64_bf16[ri][mi][si];
+        return xf32 ? qmv::qmv_wtable_b2_g128_f32[ri][mi][si] : qmv::qmv_wtable_b2_g128_bf16[ri][mi][si];
+    }
+    if (bits == 4 && gs == 64) return xf32 ? qmv::qmv_table_b4_g64_f32[ri][pi][mi][si] : qmv::qmv_table_b4_g64_bf16[ri][pi][mi][si];
+    if (bits == 4 && gs == 128) return xf32 ? qmv::qmv_table_b4_g128_f32[ri][pi][mi][si] : qmv::qmv_table_b4_g128_bf16[ri][pi][mi][si];
+    if (bits == 2 && gs == 64) return xf32 ? qmv::qmv_table_b2_g64_f32[ri][pi][mi][si] : qmv::qmv_table_b2_g64_bf16[ri][pi][mi][si];
+    return xf32 ? qmv::qmv_table_b2_g128_f32[ri][pi][mi][si] : qmv::qmv_table_b2_g128_bf16[ri][pi][mi][si];
 }
 
 struct Plan {
     Params p;
     KernelFn fn;
-    int R, W, lds, grid, blocks_per_cu;
+    int R, W, PF, lds, grid, blocks_per_cu;
 };
 
 // LDS layout and K windows.  Returns QMV_E_SHAPE if one wave step of
 // activations for all M vectors does not fit in LDS.
-int make_plan(int M, int N, int K, int bits, int gs, bool xf32, bool sbf, int R, int W, Plan& pl)
+int make_plan(int M, int N, int K, int bits, int gs, bool xf32, bool sbf, int R, int W, int PF, Plan& pl)
 {
     const int G = K / gs;
     const int lpg = gs * bits / 128;
@@ -106,6 +116,7 @@ int make_plan(int M, int N, int K, int bits, int gs, bool xf32, bool sbf, int R,
     p.G = G;
     p.chunks = chunks;
     p.nsteps = nsteps;
+    p.row_bytes = chunks * 16;
     p.win_steps = ws;
     p.nwin = nwin;
     p.n_rb = (N + W * R - 1) / (W * R);
@@ -115,14 +126,15 @@ int make_plan(int M, int N, int K, int bits, int gs, bool xf32, bool sbf, int R,
     pl.lds = p.s_off + ((s_bytes + 15) / 16) * 16;
     pl.R = R;
     pl.W = W;
-    pl.fn = pick_kernel(bits, gs, xf32, sbf, R, M);
+    pl.PF = PF;
+    pl.fn = pick_kernel(bits, gs, xf32, sbf, R, PF, M, nwin > 1);
     return QMV_OK;
 }
 
 // Per-device launch-shape cache: compute-unit count, and for each kernel
-// instance and LDS size the resident workgroups per CU (after raising the
-// instance's dynamic-LDS limit) and the instance's private (spill) bytes per
-// lane.  Filled on first use; never invalidated.
+// instance, workgroup size and LDS size the resident workgroups per CU (after
+// raising the instance's dynamic-LDS limit) and the instance's private
+// (spill) bytes per lane.  Filled on first use; never invalidated.
 struct OccEntry {
     const void* fn;
     int dev;
@@ -149,9 +161,14 @@ int cu_count_locked(int dev)
     return g_cus[dev];
 }
 
+int cu_count(int dev)
+{
+    std::lock_guard<std::mutex> lk(g_mu);
+    return cu_count_locked(dev);
+}
+
 // Resident workgroups per CU of an instance at a workgroup size and LDS size,
-// and its private bytes per lane (cached; raises the instance's dynamic-LDS
-// limit on first use).  False on a HIP error.
+// and its private bytes per lane.  False on a HIP error.
 bool occupancy(KernelFn kfn, int W, int lds, int dev, int& blocks, int& scratch)
 {
     const void* fn = reinterpret_cast<const void*>(kfn);
@@ -174,77 +191,89 @@ bool occupancy(KernelFn kfn, int W, int lds, int dev, int& blocks, int& scratch)
     return true;
 }
 
-int cu_count(int dev)
+// A candidate launch: the plan for (R, W, PF) with its grid, or false when
+// the shape has no instance or no resident workgroup.  Returns -1 on a HIP
+// error.
+int try_plan(int M, int N, int K, int bits, int gs, bool xf32, bool sbf, int R, int W, int PF,
+             int dev, int cus, Plan& pl, bool& shape_ok)
 {
-    std::lock_guard<std::mutex> lk(g_mu);
-    return cu_count_locked(dev);
+    if (make_plan(M, N, K, bits, gs, xf32, sbf, R, W, PF, pl) != QMV_OK) return 0;
+    shape_ok = true;
+    if (pl.fn == nullptr) return 0;
+    int nb = 0, scratch = 0;
+    if (!occupancy(pl.fn, W, pl.lds, dev, nb, scratch)) return -1;
+    if (nb == 0) return 0;
+    const int n_rb = pl.p.n_rb;
+    const int cap = nb * cus;
+    const int per = (n_rb + cap - 1) / cap;   // row blocks per workgroup
+    pl.grid = (n_rb + per - 1) / per;
+    pl.blocks_per_cu = nb;
+    return 1;
 }
 
-// Relative VALU issue efficiency at a number of resident wavefronts per SIMD
-// (measured on gfx950 with independent fma chains: one wavefront per SIMD
-// reaches about a third of the rate, four about 90%).
-double wave_efficiency(double wps)
-{
-    if (wps >= 8) return 1.0;
-    if (wps >= 4) return 0.87 + (wps - 4) * 0.13 / 4;
-    if (wps >= 2) return 0.60 + (wps - 2) * 0.27 / 2;
-    if (wps >= 1) return 0.31 + (wps - 1) * 0.29;
-    return 0.31 * wps;
-}
-
-// Launch shape: rows per wavefront R (given, or searched over 4, 2, 1) and
-// wavefronts per workgroup W, chosen to minimise the rows the busiest CU
-// must stream divided by the issue efficiency of its resident wavefronts.
-// The grid holds every resident workgroup (at most one per row block), and
-// each workgroup walks an equal share of the row blocks.  Instances that
-// spill registers are used only when no other instance fits.  2-bit codes
-// have no four-row instances; a request for four rows gets two.
+// Launch shape (measured on MI355X over the 12B- and 27B-class projection
+// shapes; an explicit rows-per-wavefront request is honoured in both cases):
+//   * M <= 2, bound by memory: two rows per wavefront, 8 wavefronts, one unit
+//     in flight (the best or within a few percent of the best launch on every
+//     measured shape); one row when two have no instance, fewer wavefronts
+//     when 8 do not fit.
+//   * M >= 3, bound by the vector ALUs: 8 wavefronts, one unit in flight, and
+//     the R that minimises the rows the busiest compute unit processes,
+//     weighted by the per-row cost of fewer rows per wavefront (the
+//     activations read from LDS and the decode are shared by fewer rows): 1.5x
+//     for two rows and 2.5x for one row, relative to four.
+//   * 2-bit codes have no four-row instances; K-windowed calls have one unit
+//     in flight.
 int choose_plan(int M, int N, int K, int bits, int gs, bool xf32, bool sbf, int R_req, Plan& best)
 {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return QMV_E_LAUNCH;
     const int cus = cu_count(dev);
     if (bits == 2 && R_req == 4) R_req = 2;
-    const int Rs[3] = {4, 2, 1};
-    double best_score = 0.0;
-    bool found = false, best_spills = false, shape_ok = false;
-    for (int ri = 0; ri < 3; ++ri) {
-        const int R = Rs[ri];
-        if (R_req != 0 && R != R_req) continue;
-        const int maxW = qmv::max_waves(bits, xf32, R, M);
-        for (int W = maxW; W >= 1; --W) {
-            Plan pl;
-            if (make_plan(M, N, K, bits, gs, xf32, sbf, R, W, pl) != QMV_OK) continue;
-            shape_ok = true;
-            if (pl.fn == nullptr) continue;
-            int nb = 0, scratch = 0;
-            if (!occupancy(pl.fn, W, pl.lds, dev, nb, scratch)) return QMV_E_LAUNCH;
-            if (nb == 0) continue;
-            const bool spills = scratch > 0;
-            const int n_rb = pl.p.n_rb;
-            const int cap = nb * cus;
-            const int per = (n_rb + cap - 1) / cap;          // row blocks per workgroup
-            const int grid = (n_rb + per - 1) / per;
-            const int wg_cu = (grid + cus - 1) / cus;        // workgroups on the busiest CU
-            const double rows_cu = (double)wg_cu * per * W * R;
-            const double wps = (double)std::min(nb, wg_cu) * W / 4.0;
-            double score = rows_cu / wave_efficiency(wps);
-            if (R == 1) score *= 1.25;      // x reads from LDS are not shared across rows
-            else if (R == 2) score *= 1.04;
-            const bool better = !found || (best_spills && !spills) ||
-                                (best_spills == spills && score < best_score - 1e-9);
-            if (better) {
-                found = true;
-                best_spills = spills;
-                best_score = score;
-                best = pl;
-                best.grid = grid;
-                best.blocks_per_cu = nb;
+    bool shape_ok = false;
+    auto take = [&](int R, int W, int PF) -> int {
+        if (R_req != 0 && R != R_req) return 0;
+        Plan pl;
+        const int st = try_plan(M, N, K, bits, gs, xf32, sbf, R, W, PF, dev, cus, pl, shape_ok);
+        if (st <= 0) return st;
+        best = pl;
+        return 1;
+    };
+    if (M <= 2) {
+        const int Rs[3] = {2, 1, 4};
+        for (int R : Rs)
+            for (int W = qmv::kMaxWaves; W >= 1; --W) {
+                const int st = take(R, W, 1);
+                if (st < 0) return QMV_E_LAUNCH;
+                if (st > 0) return QMV_OK;
+            }
+    } else {
+        const int Rs[3] = {4, 2, 1};
+        const double cost[3] = {1.0, 1.5, 2.5};
+        double best_score = 0.0;
+        bool found = false;
+        for (int i = 0; i < 3; ++i) {
+            const int R = Rs[i];
+            if ((R_req != 0 && R != R_req) || (bits == 2 && R == 4)) continue;
+            for (int W = qmv::kMaxWaves; W >= 1; --W) {
+                Plan pl;
+                const int st = try_plan(M, N, K, bits, gs, xf32, sbf, R, W, 1, dev, cus, pl, shape_ok);
+                if (st < 0) return QMV_E_LAUNCH;
+                if (st == 0) continue;
+                const int n_rb = pl.p.n_rb;
+                const double rows_cu = (double)((n_rb + cus - 1) / cus) * W * R;
+                const double score = rows_cu * cost[i];
+                if (!found || score < best_score - 1e-9) {
+                    found = true;
+                    best_score = score;
+                    best = pl;
+                }
+                break;
             }
         }
+        if (found) return QMV_OK;
     }
-    if (!found) return shape_ok ? QMV_E_LAUNCH : QMV_E_SHAPE;
-    return QMV_OK;
+    return shape_ok ? QMV_E_LAUNCH : QMV_E_SHAPE;
 }
 
 // Vectors per launch: all M, unless one wave step of activations for M
@@ -255,7 +284,7 @@ int vectors_per_launch(int M, int N, int K, int bits, int gs, bool xf32)
 {
     for (int mc = M; mc >= 1; --mc) {
         Plan pl;
-        if (make_plan(mc, N, K, bits, gs, xf32, true, 1, 1, pl) == QMV_OK) return mc;
+        if (make_plan(mc, N, K, bits, gs, xf32, true, 1, 1, 1, pl) == QMV_OK) return mc;
     }
     return 0;
 }
@@ -332,6 +361,7 @@ int qmv_kernel_info(int M, int N, int K, int bits, int group_size, qmv_dtype x_d
     out->waves_per_simd = std::min(pl.blocks_per_cu, (pl.grid + 255) / 256) * pl.W / 4;
     out->rows_per_wave = pl.R;
     out->k_windows = pl.p.nwin;
+    out->prefetch_units = pl.PF;
     return QMV_OK;
 }
 

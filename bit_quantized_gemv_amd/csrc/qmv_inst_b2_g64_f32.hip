@@ -3,4 +3,5 @@
 #define QMV_GS 64
 #define QMV_XF32 true
 #define QMV_TABLE qmv_table_b2_g64_f32
+#define QMV_WTABLE qmv_wtable_b2_g64_f32
 #include "qmv_inst.inc"

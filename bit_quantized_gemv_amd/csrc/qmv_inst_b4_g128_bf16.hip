@@ -3,4 +3,5 @@
 #define QMV_GS 128
 #define QMV_XF32 false
 #define QMV_TABLE qmv_table_b4_g128_bf16
+#define QMV_WTABLE qmv_wtable_b4_g128_bf16
 #include "qmv_inst.inc"

@@ -15,17 +15,26 @@
 //     1 KiB of a row contiguously.
 //   * A wavefront owns R consecutive rows (row blocking): in a step it loads the
 //     chunk of each of its rows and reads the activations of that chunk from
-//     LDS once for all R rows.  A (row block, step) pair is a unit; each
+//     LDS once for all R rows.  A (row block, step) pair is a unit.  Each
 //     wavefront keeps the weights, scales and biases of the next PF units in
-//     flight (a register ring), so HBM sees several KiB per wavefront at once.
+//     flight in a register ring; the loads of a unit are issued before the
+//     compute of the unit PF places earlier, and a scheduling barrier keeps
+//     the compiler from sinking them below it.
 //   * A workgroup of W wavefronts stages the activations x[0..M)[K-window] in
 //     LDS, together with the group sums S[m][g], and walks row blocks of W*R
-//     rows (persistent grid: staged once when the whole K fits).
+//     rows (one per workgroup when the grid fits on the chip in one round).
+//     All activation loads are issued before the first weight load, and the
+//     weight prologue is in flight while the activations are converted.
+//   * Scales and biases are loaded on every lane (each lane reads the entry of
+//     its own group); lanes other than the group's owner zero them in
+//     registers.  Rows past N and chunks past a row's end read clamped,
+//     in-bounds addresses; the activations and group sums of chunks past the
+//     row's end are zero in LDS, so those lanes add nothing.
 //   * The weight decode of a chunk happens once per step, outside the loop over
 //     the M vectors; every vector then reuses the decoded registers.
 //
 // Per-row arithmetic (fixed by K, bits, group size and activation dtype; it
-// never depends on M, R, W, the grid or the K-window size):
+// never depends on M, R, W, PF, the grid or the K-window size):
 //   1. bf16 activations: the chunk's codes become exact bf16 pairs
 //      (2^bits + q_a, 2^bits + q_b) -- the code sits in the top mantissa bits
 //      of a number in [2^bits, 2^(bits+1)) -- and D'_c is the chain of
@@ -42,7 +51,7 @@
 //      (xor-1, xor-2, ... tree).
 //   4. Each group is folded once, by its owner lane (lane % lpg == step % lpg):
 //      acc = fma(scale, D, fma(bias, S, acc)), over its groups in ascending step.
-//      Every lane executes the fold; scale and bias read as zero on the other
+//      Every lane executes the fold; scale and bias are zero on the other
 //      lanes, whose accumulators it leaves unchanged (up to the sign of a zero).
 //   5. Row total: lanes l and l ^ d combined for d = 32, 16, 8, 4, 2, 1 in that
 //      order; then round-to-nearest-even to y's dtype.
@@ -70,12 +79,13 @@ struct Params {
     int G;               // groups per row
     int chunks;          // 16-byte weight chunks per row
     int nsteps;          // wave steps per row, ceil(chunks / 64)
+    int row_bytes;       // chunks * 16
     int win_steps;       // wave steps per K window
     int nwin;            // K windows
     int n_rb;            // row blocks of W*R rows
     int y_bf16;          // y: 1 = bf16, 0 = fp32
     int x_m_bytes;       // LDS bytes of one vector's activation window (padded)
-    int gw;              // groups per K window
+    int gw;              // group sums per vector and window (win_steps * 64 / lpg)
     int s_off;           // LDS offset of S[M][gw] (fp32)
 };
 
@@ -133,14 +143,20 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c)
                                            __builtin_bit_cast(bf16x2, b), c, false);
 }
 
-// (a & mask) | magic in one v_and_or_b32.  gfx9 VALU instructions read at
-// most one scalar operand, so the mask rides in an SGPR and the magic in a
-// VGPR (the compiler would otherwise split this into v_and + v_or).
+// (a & mask) | magic.  gfx9 VOP3 instructions take no literal constants and
+// read at most one scalar operand; with the magic held in a VGPR (see
+// opaque_u32) and the mask in an SGPR this is one v_and_or_b32.
 __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t magic)
 {
-    uint32_t r;
-    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(mask), "v"(magic));
-    return r;
+    return (a & mask) | magic;
+}
+
+// v unchanged, as a value the compiler cannot fold into a constant (so a
+// constant used by a VOP3 instruction stays in a register).
+__device__ __forceinline__ uint32_t opaque_u32(uint32_t v)
+{
+    asm volatile("" : "+v"(v));
+    return v;
 }
 
 template <int BITS>
@@ -163,23 +179,25 @@ __device__ __forceinline__ uint32_t code_pair(uint32_t w, int j, uint32_t magic)
     }
 }
 
-// Buffer resources.  Loads go through raw buffer instructions: an offset at or
-// past num_records returns zero without touching memory, so masked lanes need
-// no branch and the compiler can count outstanding loads exactly.
-constexpr uint32_t kRsrcWord3 = 0x00020000u;   // gfx9-family raw buffer
-constexpr int kOut = 0x7ffffff0;               // an offset past any record count
+// Buffer resources and loads.  Every lane of every load the kernels issue
+// addresses memory inside its tensor (rows past N, lanes past a row's last
+// chunk and groups past a row's last group are clamped to the last valid
+// one), so a resource either spans all of memory (record count 0xffffffff) or
+// nothing (record count 0: a prefetch slot past the last unit, which reads
+// zero without touching memory).  Loads whose lanes fall outside the record
+// count are avoided elsewhere: on gfx950 they are not free.
+constexpr int kRsrcWord3 = 0x00020000;   // gfx9-family raw buffer
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, long long bytes)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int records)
 {
-    const long long n = bytes <= 0 ? 0 : (bytes > 0xffffffffll ? 0xffffffffll : bytes);
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)(uint32_t)n,
-                                             (int)kRsrcWord3);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, records, kRsrcWord3);
 }
 
 // 128-bit load with the non-temporal hint (weights are streamed once).
-__device__ __forceinline__ uint4 buf_load_nt(__amdgpu_buffer_rsrc_t r, int off)
+// `soff` rides in an SGPR and is added after the lane offset.
+__device__ __forceinline__ uint4 buf_load_nt(__amdgpu_buffer_rsrc_t r, int off, int soff)
 {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2);
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, 2);
     return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
@@ -187,6 +205,28 @@ __device__ __forceinline__ uint4 buf_load(__amdgpu_buffer_rsrc_t r, int off)
 {
     const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
     return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+__device__ __forceinline__ unsigned short buf_load_u16(__amdgpu_buffer_rsrc_t r, int off, int soff)
+{
+    return (unsigned short)__builtin_amdgcn_raw_buffer_load_b16(r, off, soff, 0);
+}
+
+// fp32 value of a bf16 / fp16 held in the low half of a register.  Written as
+// volatile asm so the conversion stays where the value is consumed: left to
+// the compiler it is scheduled right after the loop's previous step, which
+// makes the wavefront wait there for every load still in flight.
+__device__ __forceinline__ float bf16_to_f32_here(unsigned short h)
+{
+    float f;
+    asm volatile("v_lshlrev_b32 %0, 16, %1" : "=v"(f) : "v"(h));
+    return f;
+}
+__device__ __forceinline__ float f16_to_f32_here(unsigned short h)
+{
+    float f;
+    asm volatile("v_cvt_f32_f16 %0, %1" : "=v"(f) : "v"(h));
+    return f;
 }
 
 // Hides how an offset was computed, so the compiler keeps one unconditional
@@ -215,74 +255,61 @@ __device__ __forceinline__ int after(int v, float dep)
     return v;
 }
 
-__device__ __forceinline__ uint16_t buf_load_u16(__amdgpu_buffer_rsrc_t r, int off)
-{
-    return (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
-}
-
-// Two 16-bit loads into the halves of one register (lo from ra, hi from rb):
-// the compiler emits a d16 load and a d16_hi load into the same VGPR.
-typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint32_t buf_load_u16_pair(__amdgpu_buffer_rsrc_t ra, int oa,
-                                                      __amdgpu_buffer_rsrc_t rb, int ob)
-{
-    u16x2 v;
-    v.x = (unsigned short)__builtin_amdgcn_raw_buffer_load_b16(ra, oa, 0, 0);
-    v.y = (unsigned short)__builtin_amdgcn_raw_buffer_load_b16(rb, ob, 0, 0);
-    return __builtin_bit_cast(uint32_t, v);
-}
-
 // ------------------------------------------------------ activation staging
 // Stages x[0..M)[window] into LDS (bf16 pairs in code-pair order, or fp32 in
-// natural order) and writes S[m][group] for the window's groups.  Work is cut
-// into rounds of blockDim units (a unit = UV consecutive values of one vector);
-// load() issues a round's loads, store() consumes them, so the first round's
-// loads can be issued ahead of the weight stream.
+// natural order), writes S[m][group] for the window's groups, and zeroes the
+// activations and group sums of the window's chunks past the row's end.
+// Work is cut into units of UV consecutive values of one vector; a round is
+// one unit per thread of one vector's window.  The loads of up to XB rounds
+// are issued together before any of them is consumed.
 template <int BITS, int GS, int M, bool XF32>
 struct Stager {
     static constexpr int VPC = 128 / BITS;                    // values per weight chunk
+    static constexpr int LPG = GS * BITS / 128;               // chunks per group
+    static constexpr int XCB = VPC * (XF32 ? 4 : 2);          // LDS bytes per chunk
     static constexpr int UV = (!XF32 && BITS == 2) ? 16 : 8;  // values per unit
     static constexpr int UPG = GS / UV;                       // units per group
     static constexpr int NLD = (XF32 || BITS == 2) ? 2 : 1;   // 16-byte loads per unit
-    static constexpr int NRB = (M >= 8) ? 8 : (M >= 3 ? 4 : 2);  // rounds whose loads are in flight together
+    static constexpr int XB = ((M <= 2) ? 4 : (M <= 6 ? 8 : 16)) / NLD;  // rounds in flight
 
-    int units_per_m, total, rounds, k_lo;
+    int upm;      // units per vector in this window
+    int rpm;      // rounds per vector
+    int rounds;   // M * rpm
+    int k_lo;     // first value of the window
+    int c_n;      // chunks in this window
 
     __device__ void begin(const Params& p, int win)
     {
         const int c_lo = win * p.win_steps * kWave;
-        const int c_hi = min(p.chunks, c_lo + p.win_steps * kWave);
-        units_per_m = (c_hi - c_lo) * VPC / UV;
-        total = units_per_m * M;
-        rounds = (total + (int)blockDim.x - 1) / (int)blockDim.x;
+        c_n = min(p.chunks - c_lo, p.win_steps * kWave);
+        upm = c_n * VPC / UV;
+        rpm = (upm + (int)blockDim.x - 1) / (int)blockDim.x;
+        rounds = M * rpm;
         k_lo = c_lo * VPC;
     }
 
-    // unit handled by this thread in round `round`
-    __device__ void where(int round, int& m, int& l, bool& valid) const
+    // vector and unit of this thread in round i (m is wave-uniform)
+    __device__ void where(int i, int& m, int& l) const
     {
-        const int u = round * (int)blockDim.x + (int)threadIdx.x;
-        valid = u < total;
-        m = valid ? u / units_per_m : 0;
-        l = valid ? u - m * units_per_m : 0;
+        m = (M == 1) ? 0 : i / rpm;
+        l = (i - m * rpm) * (int)blockDim.x + (int)threadIdx.x;
     }
 
-    // issue the loads of one round (all threads issue; masked lanes read nothing)
-    __device__ void load(const Params& p, __amdgpu_buffer_rsrc_t xr, int round, uint4 (&d)[NLD]) const
+    __device__ void load(const Params& p, __amdgpu_buffer_rsrc_t xr, int i, uint4 (&d)[NLD]) const
     {
         int m, l;
-        bool valid;
-        where(round, m, l, valid);
-        const int off = opaque(valid ? (m * p.K + k_lo + l * UV) * (XF32 ? 4 : 2) : kOut);
+        where(i, m, l);
+        const int lc = min(l, upm - 1);     // threads past the window re-read its last unit
+        const int off = (m * p.K + k_lo + lc * UV) * (XF32 ? 4 : 2);
 #pragma unroll
-        for (int i = 0; i < NLD; ++i) d[i] = buf_load(xr, off + 16 * i);
+        for (int k = 0; k < NLD; ++k) d[k] = buf_load(xr, off + 16 * k);
     }
 
-    __device__ void store(const Params& p, uint8_t* lds, int round, const uint4 (&d)[NLD]) const
+    __device__ void store(const Params& p, uint8_t* lds, int i, const uint4 (&d)[NLD]) const
     {
         int m, l;
-        bool valid;
-        where(round, m, l, valid);
+        where(i, m, l);
+        const bool valid = l < upm;
         float* S = reinterpret_cast<float*>(lds + p.s_off);
         uint8_t* dst = lds + m * p.x_m_bytes;
         float part;
@@ -293,7 +320,7 @@ struct Stager {
                                 __uint_as_float(d[1].z), __uint_as_float(d[1].w)};
             part = v[0];
 #pragma unroll
-            for (int i = 1; i < 8; ++i) part = part + v[i];
+            for (int k = 1; k < 8; ++k) part = part + v[k];
             if (valid) {
                 *reinterpret_cast<uint4*>(dst + lds_phys(l * 32)) = d[0];
                 *reinterpret_cast<uint4*>(dst + lds_phys(l * 32 + 16)) = d[1];
@@ -306,7 +333,7 @@ struct Stager {
                                 bf16_bits_to_f32(q0.w & 0xffffu), bf16_bits_to_f32(q0.w >> 16)};
             part = v[0];
 #pragma unroll
-            for (int i = 1; i < 8; ++i) part = part + v[i];
+            for (int k = 1; k < 8; ++k) part = part + v[k];
             if (valid) {
                 // pairs (x_j, x_{j+4}), j = 0..3
                 uint4 q;
@@ -321,16 +348,16 @@ struct Stager {
             float pa = bf16_bits_to_f32(dw[0] & 0xffffu);
             pa = pa + bf16_bits_to_f32(dw[0] >> 16);
 #pragma unroll
-            for (int i = 1; i < 4; ++i) {
-                pa = pa + bf16_bits_to_f32(dw[i] & 0xffffu);
-                pa = pa + bf16_bits_to_f32(dw[i] >> 16);
+            for (int k = 1; k < 4; ++k) {
+                pa = pa + bf16_bits_to_f32(dw[k] & 0xffffu);
+                pa = pa + bf16_bits_to_f32(dw[k] >> 16);
             }
             float pb = bf16_bits_to_f32(dw[4] & 0xffffu);
             pb = pb + bf16_bits_to_f32(dw[4] >> 16);
 #pragma unroll
-            for (int i = 5; i < 8; ++i) {
-                pb = pb + bf16_bits_to_f32(dw[i] & 0xffffu);
-                pb = pb + bf16_bits_to_f32(dw[i] >> 16);
+            for (int k = 5; k < 8; ++k) {
+                pb = pb + bf16_bits_to_f32(dw[k] & 0xffffu);
+                pb = pb + bf16_bits_to_f32(dw[k] >> 16);
             }
             part = pa + pb;
             if (valid) {
@@ -346,38 +373,48 @@ struct Stager {
                 *reinterpret_cast<uint4*>(dst + lds_phys(l * 32 + 16)) = make_uint4(pr[4], pr[5], pr[6], pr[7]);
             }
         }
-        // group sum: the UPG units of a group sit in UPG adjacent lanes
+        // group sum: the UPG units of a group sit in UPG adjacent lanes (a
+        // round starts at a multiple of the wavefront size and a window holds
+        // whole groups, so the lanes past the window form whole groups too)
         part = lane_group_sum<UPG>(part);
         if (valid && (l % UPG) == 0) S[m * p.gw + l / UPG] = part;
     }
 
-    // Stage a window: the loads of up to NRB rounds are issued together, then
-    // stored.  `between` runs after the first batch's loads are issued by every
-    // wavefront of the workgroup (a barrier orders them): the caller issues its
-    // weight prefetch there, so the activation requests sit ahead of the
-    // weight stream in the compute unit's queue and both overlap.
+    // zero the activations and group sums of the window's chunks past the
+    // row's end (only the last window of a row has them)
+    __device__ void zero_tail(const Params& p, uint8_t* lds) const
+    {
+        const int pieces = (p.win_steps * kWave - c_n) * XCB / 16;
+        const int groups = p.gw - c_n / LPG;
+        float* S = reinterpret_cast<float*>(lds + p.s_off);
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            for (int j = (int)threadIdx.x; j < pieces; j += (int)blockDim.x)
+                *reinterpret_cast<uint4*>(lds + m * p.x_m_bytes + lds_phys(c_n * XCB + 16 * j)) =
+                    make_uint4(0, 0, 0, 0);
+            for (int j = (int)threadIdx.x; j < groups; j += (int)blockDim.x)
+                S[m * p.gw + c_n / LPG + j] = 0.0f;
+        }
+    }
+
+    // Stage a window.  `between` runs after the first batch of activation
+    // loads is issued (the caller issues its weight prologue there, so the
+    // activation requests are ahead of the weight stream).
     template <class F>
     __device__ void stage(const Params& p, __amdgpu_buffer_rsrc_t xr, uint8_t* lds, int win, F&& between)
     {
         begin(p, win);
-        {
-            uint4 d[NRB][NLD];
+        for (int r0 = 0; r0 < rounds; r0 += XB) {
+            uint4 d[XB][NLD];
 #pragma unroll
-            for (int i = 0; i < NRB; ++i) load(p, xr, i, d[i]);
-            __syncthreads();
-            between();
+            for (int i = 0; i < XB; ++i)
+                if (r0 + i < rounds) load(p, xr, r0 + i, d[i]);
+            if (r0 == 0) between();
 #pragma unroll
-            for (int i = 0; i < NRB; ++i)
-                if (i < rounds) store(p, lds, i, d[i]);
-        }
-        for (int r0 = NRB; r0 < rounds; r0 += NRB) {
-            uint4 d[NRB][NLD];
-#pragma unroll
-            for (int i = 0; i < NRB; ++i) load(p, xr, r0 + i, d[i]);
-#pragma unroll
-            for (int i = 0; i < NRB; ++i)
+            for (int i = 0; i < XB; ++i)
                 if (r0 + i < rounds) store(p, lds, r0 + i, d[i]);
         }
+        zero_tail(p, lds);
     }
 };
 
@@ -472,25 +509,30 @@ __device__ __forceinline__ int reduce_index(int lane)
 }
 
 // ------------------------------------------------------------------- kernel
-// Units in flight per wavefront (weight loads issued ahead of use).
-constexpr int prefetch_depth(int R, int M) { return (R * M <= 2) ? 4 : (R * M <= 8 ? 2 : 1); }
+// Largest workgroup (in wavefronts) an instance is compiled for.
+constexpr int kMaxWaves = 8;
 
-// Largest workgroup (in wavefronts) an instance is compiled for: 16 when its
-// registers fit four wavefronts per SIMD (4-bit codes, bf16 activations, few
-// rows x vectors), else 8.
-constexpr int max_waves(int BITS, bool XF32, int R, int M)
+// Resident wavefronts per SIMD an instance asks the register allocator for:
+// eight (at most 64 VGPRs) for the memory-bound 4-bit, bf16-activation,
+// one-vector instances with at most two rows, one unit in flight and no K
+// windows, so a grid of one workgroup per row block is resident in one round;
+// else no constraint.
+constexpr int waves_hint(int BITS, bool XF32, int R, int M, int PF, bool WIN)
 {
-    return (BITS == 4 && !XF32 && R * M <= 4) ? 16 : 8;
+    return (BITS == 4 && !XF32 && M == 1 && R <= 2 && PF == 1 && !WIN) ? 8 : 1;
 }
 
-template <int BITS, int GS, int R, int M, bool XF32, bool SBF>
-__global__ __launch_bounds__(max_waves(BITS, XF32, R, M) * kWave) void qmv_affine_kernel(const Params p)
+// WIN: the instance restages the activations per K window (when x[0..M)[0..K)
+// does not fit in LDS); instances without it require p.nwin == 1.
+template <int BITS, int GS, int R, int M, int PF, bool XF32, bool SBF, bool WIN>
+__global__ __launch_bounds__(kMaxWaves * kWave) __attribute__((amdgpu_waves_per_eu(waves_hint(BITS, XF32, R, M, PF, WIN))))
+void qmv_affine_kernel(const Params p)
 {
     constexpr int LPG = GS * BITS / 128;          // lanes (chunks) per group
     constexpr int VPC = 128 / BITS;               // values per chunk
     constexpr int XCB = VPC * (XF32 ? 4 : 2);     // activation bytes per chunk in LDS
+    constexpr int XSTEP = kWave * XCB + kWave * XCB / 16;  // padded LDS bytes per wave step
     constexpr int OFFSET = 1 << BITS;             // code offset of the bf16 pairs
-    constexpr int PF = prefetch_depth(R, M);      // units in flight
     constexpr int NS = PF + 1;                    // ring slots
     constexpr int V = R * M;
     constexpr int P = pow2_at_least(V);
@@ -499,119 +541,132 @@ __global__ __launch_bounds__(max_waves(BITS, XF32, R, M) * kWave) void qmv_affin
     extern __shared__ __align__(16) uint8_t lds[];
     const int lane = threadIdx.x & (kWave - 1);
     // wave-uniform by construction; readfirstlane lets the compiler keep it
-    // (and every buffer descriptor built from it) in scalar registers
+    // (and everything derived from it) in scalar registers
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
     const int W = blockDim.x / kWave;
+    const int grid = gridDim.x;
     const float* Slds = reinterpret_cast<const float*>(lds + p.s_off);
-    const int row_bytes = p.chunks * 16;
 
     if ((int)blockIdx.x >= p.n_rb) return;
-    const int n_my = (p.n_rb - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+    const int n_my = (p.n_rb - 1 - (int)blockIdx.x) / grid + 1;   // row blocks of this workgroup
     const int n_units = n_my * p.nsteps;
-    const __amdgpu_buffer_rsrc_t xr =
-        make_rsrc(p.x, (long long)M * p.K * (XF32 ? 4 : 2));
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(p.x, M * p.K * (XF32 ? 4 : 2));
 
     // Units are issued in order: unit (irb, it) is row block
-    // blockIdx.x + irb * gridDim.x, wave step it.  Buffer resources start at the
-    // wavefront's first row, so rows past N fall outside the record count and
-    // read as zero.  Every call issues the same 3R loads; units past the last
-    // one (irb >= n_my) get empty resources and read nothing.
-    int it = 0, irb = 0;
-    auto issue = [&](uint4 (&wv)[R], uint32_t (&sbv)[R]) {
-        const int row0 = (((int)blockIdx.x + irb * (int)gridDim.x) * W + wave) * R;
-        const long long rows_left = (irb < n_my) ? (long long)p.N - row0 : 0;
-        const __amdgpu_buffer_rsrc_t wr =
-            make_rsrc(reinterpret_cast<const uint8_t*>(p.w) + (size_t)row0 * row_bytes, rows_left * row_bytes);
-        const __amdgpu_buffer_rsrc_t sr = make_rsrc(p.s + (size_t)row0 * p.G, rows_left * p.G * 2);
-        const __amdgpu_buffer_rsrc_t br = make_rsrc(p.b + (size_t)row0 * p.G, rows_left * p.G * 2);
-        const int c = it * kWave + lane;
-        const bool active = c < p.chunks;
-        // scale and bias are read by the group's owner lane only; on every other
-        // lane they read as zero, which turns its fold into a no-op
-        const bool own = active && ((lane % LPG) == (it % LPG));
-        const uint32_t wo = (uint32_t)opaque(active ? c * 16 : kOut);
-        const uint32_t mo = (uint32_t)opaque(own ? (c / LPG) * 2 : kOut);
+    // blockIdx.x + irb * gridDim.x, wave step it.  Rows past N read row N-1;
+    // a lane past the row's last chunk (group) reads the last chunk (group).
+    // Slots past the last unit get an empty resource and read nothing.  The
+    // resources and row offsets of the row block being issued live in scalar
+    // registers and are rebuilt only when the issue moves to the next block;
+    // the lane offsets advance by one step per issue.
+    int is_t = 0, is_rb = 0;
+    int i_row0 = ((int)blockIdx.x * W + wave) * R;   // first row of the block being issued
+    const int row_step = grid * W * R;
+    __amdgpu_buffer_rsrc_t i_wr, i_sr, i_br;
+    int i_sw[R], i_ss[R];                            // per-row scalar offsets (weights, scales/biases)
+    auto set_block = [&]() {
+        // every input of the resources is wave-uniform; readfirstlane makes that
+        // explicit (a resource the compiler cannot prove uniform costs a
+        // waterfall loop around every load)
+        const int rbase = __builtin_amdgcn_readfirstlane(min(i_row0, p.N - 1));
+        const int records = __builtin_amdgcn_readfirstlane((is_rb < n_my) ? -1 : 0);
+        i_wr = make_rsrc(reinterpret_cast<const uint8_t*>(p.w) + (size_t)rbase * p.row_bytes, records);
+        i_sr = make_rsrc(p.s + (size_t)rbase * p.G, records);
+        i_br = make_rsrc(p.b + (size_t)rbase * p.G, records);
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            wv[r] = buf_load_nt(wr, (int)(wo + (uint32_t)(r * row_bytes)));
-            const int o = (int)(mo + (uint32_t)(r * p.G * 2));
-            sbv[r] = buf_load_u16_pair(sr, o, br, o);
+            const int rr = min(r, p.N - 1 - rbase);
+            i_sw[r] = rr * p.row_bytes;
+            i_ss[r] = rr * p.G * 2;
         }
-        if (++it == p.nsteps) {
-            it = 0;
-            ++irb;
+    };
+    set_block();
+    const int wo0 = lane * 16;                       // lane's chunk offset in a row's first step
+    const int mo0 = (lane / LPG) * 2;                // lane's group offset in a row's first step
+    int i_wo = wo0, i_mo = mo0;
+    const int wo_max = p.row_bytes - 16, mo_max = p.G * 2 - 2;
+    auto issue = [&](uint4 (&wv)[R], unsigned short (&sv)[R], unsigned short (&bv)[R]) {
+        const int wo = min(i_wo, wo_max);
+        const int mo = min(i_mo, mo_max);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            wv[r] = buf_load_nt(i_wr, wo, i_sw[r]);
+            sv[r] = buf_load_u16(i_sr, mo, i_ss[r]);
+            bv[r] = buf_load_u16(i_br, mo, i_ss[r]);
+        }
+        if (++is_t == p.nsteps) {
+            is_t = 0;
+            ++is_rb;
+            i_row0 += row_step;
+            set_block();
+            i_wo = wo0;
+            i_mo = mo0;
+        } else {
+            i_wo += kWave * 16;
+            i_mo += (kWave / LPG) * 2;
         }
     };
 
-    const uint32_t magic = code_magic<BITS>();
+    const uint32_t magic = opaque_u32(code_magic<BITS>());
     Stager<BITS, GS, M, XF32> stg;
     uint4 wb[NS][R];
-    uint32_t sbb[NS][R];    // scale (low half) and bias (high half) bits
+    unsigned short sb[NS][R], bb[NS][R];    // scale and bias bits
     auto prologue = [&]() {
 #pragma unroll
-        for (int s = 0; s < PF; ++s) issue(wb[s], sbb[s]);
+        for (int s = 0; s < PF; ++s) issue(wb[s], sb[s], bb[s]);
     };
-    if (p.nwin == 1) {
-        // stage the whole activation tile; the weight prefetch is issued right
-        // after the first batch of activation loads
-        stg.stage(p, xr, lds, 0, prologue);
-        __syncthreads();
-    } else {
-        prologue();
-    }
+    // activation loads first, then the weight prologue, then the conversion
+    stg.stage(p, xr, lds, 0, prologue);
+    __syncthreads();
 
     float acc[R][M];
-    int t = 0, rbi = 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
+    int c_rb = 0, c_t = 0, c_tw = 0, c_win = 0;   // unit consumed next; its step within the window
+    const int xl = lds_phys(lane * XCB);          // LDS offset of the lane's chunk in a window's first step
+    const int gl0 = lane / LPG;                   // group of the lane's chunk in a window's first step
     for (int ub = 0; ub < n_units; ub += NS) {
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
-            const int u = ub + s;
-            if (u < n_units) {
-                // the slot consumed one unit ago takes the unit PF ahead
-                issue(wb[(s + PF) % NS], sbb[(s + PF) % NS]);
-                if (t == 0) {
-#pragma unroll
-                    for (int r = 0; r < R; ++r)
-#pragma unroll
-                        for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
-                }
-                if (p.nwin > 1 && (t % p.win_steps) == 0) {
-                    __syncthreads();
-                    stg.stage(p, xr, lds, t / p.win_steps, [] {});
-                    __syncthreads();
+            // the slot consumed one unit ago takes the unit PF ahead
+            issue(wb[(s + PF) % NS], sb[(s + PF) % NS], bb[(s + PF) % NS]);
+            __builtin_amdgcn_sched_barrier(0);
+            if (ub + s < n_units) {
+                const int t = c_t;
+                if constexpr (WIN) {
+                    if (c_tw == p.win_steps) {
+                        c_tw = 0;
+                        ++c_win;
+                    }
+                    if (c_tw == 0 && (c_rb > 0 || t > 0)) {
+                        // K windows: restage this window (the first one was staged above)
+                        __syncthreads();
+                        stg.stage(p, xr, lds, c_win, [] {});
+                        __syncthreads();
+                    }
                 }
                 const uint4 (&wcur)[R] = wb[s];
-                // Scale and bias of each row's group: zero on every lane but the
+                // scale and bias of each row's group: zero on every lane but the
                 // group's owner, so the fold acc = s*D + (b*S + acc) leaves a
-                // non-owner's accumulator unchanged without a branch.
+                // non-owner's accumulator unchanged without a branch
+                const bool own = (lane % LPG) == (t % LPG);
                 float sv[R], bv[R];
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
-                    const uint32_t v = sbb[s][r];
-                    sv[r] = SBF ? __uint_as_float(v << 16) : f16_bits_to_f32(v & 0xffffu);
-                    bv[r] = SBF ? __uint_as_float(v & 0xffff0000u) : f16_bits_to_f32(v >> 16);
+                    const float fs = SBF ? bf16_to_f32_here(sb[s][r]) : f16_to_f32_here(sb[s][r]);
+                    const float fb = SBF ? bf16_to_f32_here(bb[s][r]) : f16_to_f32_here(bb[s][r]);
+                    sv[r] = own ? fs : 0.0f;
+                    bv[r] = own ? fb : 0.0f;
                 }
-
-                const int win = t / p.win_steps;
-                const int t_lo = win * p.win_steps;
-                const int c = t * kWave + lane;              // chunk of this lane
-                const bool active = c < p.chunks;
-                const int grp = active ? c / LPG : 0;        // group of the chunk
-                const int gl = active ? grp - win * p.gw : 0;  // group within the window
-                // chunk within the window; a lane past the last chunk reads the
-                // window's first chunk (staged, finite values; its weights read as
-                // zero and its scale and bias too, so its fold adds nothing)
-                const int cl = active ? c - t_lo * kWave : 0;
+                const int gl = c_tw * (kWave / LPG) + gl0;    // group within the window
+                const int xo0 = xl + c_tw * XSTEP;            // chunk's LDS offset (never straddles padding)
 
                 if constexpr (!XF32) {
                     // ---- bf16 activations: exact code pairs and v_dot2_f32_bf16
                     constexpr int NP = 64 / BITS;              // code pairs per chunk
                     constexpr int PPW = 16 / BITS;             // pairs per word
-                    // activation pairs of vector m for this lane's chunk, and the group's
-                    // sum.  xo is the chunk's LDS offset lds_phys(cl * XCB), possibly tied
-                    // to an earlier result by after(); a chunk never straddles a padding
-                    // point, so its 16-byte pieces sit at xo + 16 v.
-                    const int xo0 = lds_phys(cl * XCB);
                     auto read_x = [&](int m, int xo, uint32_t (&xp)[NP], float& S) {
                         const uint8_t* xs = lds + m * p.x_m_bytes + xo;
                         S = Slds[m * p.gw + gl];
@@ -642,17 +697,37 @@ __global__ __launch_bounds__(max_waves(BITS, XF32, R, M) * kWave) void qmv_affin
                     };
                     if constexpr (M <= R) {
                         // few vectors: activation pairs of all M vectors first, then one
-                        // row at a time (decode, then every vector's chain and fold)
+                        // row at a time, one weight word at a time: decode the word's
+                        // pairs and extend every vector's chain with them (the same chain
+                        // order as decoding the whole chunk first; only the pairs of one
+                        // word are live at once)
                         uint32_t xp[M][NP];
                         float S[M];
 #pragma unroll
                         for (int m = 0; m < M; ++m) read_x(m, xo0, xp[m], S[m]);
 #pragma unroll
                         for (int r = 0; r < R; ++r) {
-                            uint32_t qp[NP];
-                            decode(wcur[r], qp);
+                            const uint32_t wd[4] = {wcur[r].x, wcur[r].y, wcur[r].z, wcur[r].w};
+                            float d[M];
 #pragma unroll
-                            for (int m = 0; m < M; ++m) chain_fold(qp, xp[m], S[m], r, acc[r][m]);
+                            for (int m = 0; m < M; ++m) d[m] = 0.0f;
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                uint32_t qw[PPW];
+#pragma unroll
+                                for (int j = 0; j < PPW; ++j) qw[j] = code_pair<BITS>(wd[i], j, magic);
+#pragma unroll
+                                for (int m = 0; m < M; ++m)
+#pragma unroll
+                                    for (int j = 0; j < PPW; ++j) d[m] = dot2(qw[j], xp[m][i * PPW + j], d[m]);
+                                __builtin_amdgcn_sched_barrier(0);
+                            }
+#pragma unroll
+                            for (int m = 0; m < M; ++m) {
+                                float dd = lane_group_sum<LPG>(d[m]);
+                                dd = __builtin_fmaf(-(float)OFFSET, S[m], dd);
+                                acc[r][m] = pinned(__builtin_fmaf(sv[r], dd, __builtin_fmaf(bv[r], S[m], acc[r][m])));
+                            }
                         }
                     } else {
                         // many vectors: decode every row once, then one vector at a time.
@@ -685,7 +760,6 @@ __global__ __launch_bounds__(max_waves(BITS, XF32, R, M) * kWave) void qmv_affin
                     constexpr int VPW = 32 / BITS;             // values per word
                     float dsum[R][M];
                     float xq[2][VPW];
-                    const int xo0 = lds_phys(cl * XCB);      // a chunk never straddles padding
                     auto read_x = [&](int k, int xo, float (&xv)[VPW]) {
                         const int i = k / M, m = k % M;
                         const uint8_t* xs = lds + m * p.x_m_bytes + xo + i * VPW * 4;
@@ -744,7 +818,7 @@ __global__ __launch_bounds__(max_waves(BITS, XF32, R, M) * kWave) void qmv_affin
                     for (int i = 0; i < P; ++i) v[i] = (i < V) ? acc[i / M][i % M] : 0.0f;
                     lane_reduce<P>(v, lane);
                     const int idx = reduce_index<P>(lane);
-                    const int row0 = (((int)blockIdx.x + rbi * (int)gridDim.x) * W + wave) * R;
+                    const int row0 = (((int)blockIdx.x + c_rb * grid) * W + wave) * R;
                     const int r = idx / M, m = idx - (idx / M) * M;
                     if ((lane % (64 / P)) == 0 && idx < V && row0 + r < p.N) {
                         const size_t o = (size_t)m * p.N + row0 + r;
@@ -753,10 +827,17 @@ __global__ __launch_bounds__(max_waves(BITS, XF32, R, M) * kWave) void qmv_affin
                         else
                             static_cast<float*>(p.y)[o] = v[0];
                     }
-                    t = 0;
-                    ++rbi;
+#pragma unroll
+                    for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+                        for (int mm = 0; mm < M; ++mm) acc[rr][mm] = 0.0f;
+                    c_t = 0;
+                    c_tw = 0;
+                    c_win = 0;
+                    ++c_rb;
                 } else {
-                    ++t;
+                    ++c_t;
+                    ++c_tw;
                 }
             }
         }

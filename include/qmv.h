@@ -114,7 +114,9 @@ int qmv_affine_ex(const uint32_t* w_packed, const void* scales, const void* bias
  * scratch_bytes (private memory per lane; 0 = no register spills), lds_bytes
  * per workgroup (dynamic), wg_size (threads), grid (workgroups),
  * waves_per_simd (resident waves per SIMD at this LDS/VGPR use), rows_per_wave,
- * k_windows (K windows the activation tile is staged in; 1 = whole K). */
+ * k_windows (K windows the activation tile is staged in; 1 = whole K),
+ * prefetch_units (units of R rows x one 64-lane step whose loads each
+ * wavefront keeps in flight). */
 typedef struct {
     int vgprs;
     int scratch_bytes;
@@ -124,6 +126,7 @@ typedef struct {
     int waves_per_simd;
     int rows_per_wave;
     int k_windows;
+    int prefetch_units;
 } qmv_kernel_info_t;
 
 int qmv_kernel_info(int M, int N, int K, int bits, int group_size, qmv_dtype x_dt,
