@@ -288,27 +288,22 @@ struct Stager {
         k_lo = c_lo * VPC;
     }
 
-    // vector and unit of this thread in round i (m is wave-uniform)
-    __device__ void where(int i, int& m, int& l) const
+    // Loads of the round (vector m, j-th round of that vector).  Threads past
+    // the window, and rounds past the last (m >= M), re-read an in-bounds
+    // unit; their data is not stored.
+    __device__ void load(const Params& p, __amdgpu_buffer_rsrc_t xr, int m, int j, uint4 (&d)[NLD]) const
     {
-        m = (M == 1) ? 0 : i / rpm;
-        l = (i - m * rpm) * (int)blockDim.x + (int)threadIdx.x;
-    }
-
-    __device__ void load(const Params& p, __amdgpu_buffer_rsrc_t xr, int i, uint4 (&d)[NLD]) const
-    {
-        int m, l;
-        where(i, m, l);
-        const int lc = min(l, upm - 1);     // threads past the window re-read its last unit
-        const int off = (m * p.K + k_lo + lc * UV) * (XF32 ? 4 : 2);
+        const int l = j * (int)blockDim.x + (int)threadIdx.x;
+        const int lc = min(l, upm - 1);
+        const int mc = min(m, M - 1);
+        const int off = (mc * p.K + k_lo + lc * UV) * (XF32 ? 4 : 2);
 #pragma unroll
         for (int k = 0; k < NLD; ++k) d[k] = buf_load(xr, off + 16 * k);
     }
 
-    __device__ void store(const Params& p, uint8_t* lds, int i, const uint4 (&d)[NLD]) const
+    __device__ void store(const Params& p, uint8_t* lds, int m, int j, const uint4 (&d)[NLD]) const
     {
-        int m, l;
-        where(i, m, l);
+        const int l = j * (int)blockDim.x + (int)threadIdx.x;
         const bool valid = l < upm;
         float* S = reinterpret_cast<float*>(lds + p.s_off);
         uint8_t* dst = lds + m * p.x_m_bytes;
@@ -397,22 +392,44 @@ struct Stager {
         }
     }
 
-    // Stage a window.  `between` runs after the first batch of activation
-    // loads is issued (the caller issues its weight prologue there, so the
-    // activation requests are ahead of the weight stream).
+    // Stage a window.  The loads of the first XB rounds are issued together,
+    // unconditionally (so the compiler counts the loads in flight exactly);
+    // `between` runs next (the caller issues its weight prologue there, so the
+    // activation requests are ahead of the weight stream); then those rounds
+    // are converted and stored.  Rounds past XB (long windows only) are
+    // loaded and stored one at a time afterwards.
     template <class F>
     __device__ void stage(const Params& p, __amdgpu_buffer_rsrc_t xr, uint8_t* lds, int win, F&& between)
     {
         begin(p, win);
-        for (int r0 = 0; r0 < rounds; r0 += XB) {
+        {
             uint4 d[XB][NLD];
+            int m = 0, j = 0;
 #pragma unroll
-            for (int i = 0; i < XB; ++i)
-                if (r0 + i < rounds) load(p, xr, r0 + i, d[i]);
-            if (r0 == 0) between();
+            for (int i = 0; i < XB; ++i) {
+                load(p, xr, m, j, d[i]);
+                if (++j == rpm) {
+                    j = 0;
+                    ++m;
+                }
+            }
+            between();
+            m = 0;
+            j = 0;
 #pragma unroll
-            for (int i = 0; i < XB; ++i)
-                if (r0 + i < rounds) store(p, lds, r0 + i, d[i]);
+            for (int i = 0; i < XB; ++i) {
+                if (i < rounds) store(p, lds, m, j, d[i]);
+                if (++j == rpm) {
+                    j = 0;
+                    ++m;
+                }
+            }
+        }
+        for (int i = XB; i < rounds; ++i) {
+            const int m = i / rpm, j = i - (i / rpm) * rpm;
+            uint4 d[NLD];
+            load(p, xr, m, j, d);
+            store(p, lds, m, j, d);
         }
         zero_tail(p, lds);
     }
