@@ -276,17 +276,23 @@ int choose_plan(int M, int N, int K, int bits, int gs, bool xf32, bool sbf, int 
     return shape_ok ? QMV_E_LAUNCH : QMV_E_SHAPE;
 }
 
-// Vectors per launch: all M, unless one wave step of activations for M
-// vectors does not fit in LDS (fp32 activations with 2-bit codes); then the
-// largest count that fits.  Vectors are independent, so splitting M changes
-// no result bit.
+// Vectors per launch: at most QMV_TILE_M, and at most as many as one wave
+// step of activations of fits in LDS (fewer only for fp32 activations with
+// 2-bit codes); the M vectors are then cut into equal tiles of at most that
+// many.  Vectors are independent, so tiling M changes no result bit.
 int vectors_per_launch(int M, int N, int K, int bits, int gs, bool xf32)
 {
-    for (int mc = M; mc >= 1; --mc) {
+    int cap = 0;
+    for (int mc = std::min(M, QMV_TILE_M); mc >= 1; --mc) {
         Plan pl;
-        if (make_plan(mc, N, K, bits, gs, xf32, true, 1, 1, 1, pl) == QMV_OK) return mc;
+        if (make_plan(mc, N, K, bits, gs, xf32, true, 1, 1, 1, pl) == QMV_OK) {
+            cap = mc;
+            break;
+        }
     }
-    return 0;
+    if (cap == 0) return 0;
+    const int tiles = (M + cap - 1) / cap;
+    return (M + tiles - 1) / tiles;
 }
 
 }  // namespace

@@ -45,14 +45,18 @@
 //      ascending k, from 0, with exact fp32 codes.
 //   2. The lpg = gs*bits/128 chunks of a group sit in adjacent lanes; their
 //      partials are combined by a DPP butterfly (xor 1, then xor 2).
-//   3. D = D' - 2^bits * S (bf16 path; exact offset removal up to one rounding),
-//      D = D' (fp32 path).  S[m][g] is the fp32 sum of the group's activations:
-//      8-value blocks summed left to right, blocks combined pairwise
-//      (xor-1, xor-2, ... tree).
+//   3. S[m][g] is the fp32 sum of the group's activations.  bf16 activations:
+//      each 8-value block (16 at 2 bits) is a v_dot2_f32_bf16 chain of its
+//      natural pairs (x_2i, x_2i+1) against (1, 1) from 0 (at 2 bits two
+//      8-value chains, then added); fp32 activations: 8-value blocks summed
+//      left to right.  Blocks are combined pairwise (xor-1, xor-2, ... tree).
 //   4. Each group is folded once, by its owner lane (lane % lpg == step % lpg):
-//      acc = fma(scale, D, fma(bias, S, acc)), over its groups in ascending step.
-//      Every lane executes the fold; scale and bias are zero on the other
-//      lanes, whose accumulators it leaves unchanged (up to the sign of a zero).
+//      acc = fma(scale, D', fma(bias', S, acc)), over its groups in ascending
+//      step, where bias' = fma(-2^bits, scale, bias) for bf16 activations (D'
+//      carries the code offset: scale*D' + bias'*S = scale*D + bias*S in exact
+//      arithmetic) and bias' = bias for fp32 activations.  Every lane executes
+//      the fold; scale and bias are zero on the other lanes, whose
+//      accumulators it leaves unchanged (up to the sign of a zero).
 //   5. Row total: lanes l and l ^ d combined for d = 32, 16, 8, 4, 2, 1 in that
 //      order; then round-to-nearest-even to y's dtype.
 #pragma once
@@ -262,6 +266,8 @@ __device__ __forceinline__ int after(int v, float dep)
 // Work is cut into units of UV consecutive values of one vector; a round is
 // one unit per thread of one vector's window.  The loads of up to XB rounds
 // are issued together before any of them is consumed.
+constexpr uint32_t kOnePair = 0x3f803f80u;   // bf16 pair (1.0, 1.0)
+
 template <int BITS, int GS, int M, bool XF32>
 struct Stager {
     static constexpr int VPC = 128 / BITS;                    // values per weight chunk
@@ -321,49 +327,40 @@ struct Stager {
                 *reinterpret_cast<uint4*>(dst + lds_phys(l * 32 + 16)) = d[1];
             }
         } else if constexpr (BITS == 4) {
+            // sum: a v_dot2_f32_bf16 chain of the unit's four natural pairs
+            // (x_2i, x_2i+1) against (1, 1), from 0
             const uint4 q0 = d[0];
-            const float v[8] = {bf16_bits_to_f32(q0.x & 0xffffu), bf16_bits_to_f32(q0.x >> 16),
-                                bf16_bits_to_f32(q0.y & 0xffffu), bf16_bits_to_f32(q0.y >> 16),
-                                bf16_bits_to_f32(q0.z & 0xffffu), bf16_bits_to_f32(q0.z >> 16),
-                                bf16_bits_to_f32(q0.w & 0xffffu), bf16_bits_to_f32(q0.w >> 16)};
-            part = v[0];
-#pragma unroll
-            for (int k = 1; k < 8; ++k) part = part + v[k];
+            part = dot2(q0.x, kOnePair, 0.0f);
+            part = dot2(q0.y, kOnePair, part);
+            part = dot2(q0.z, kOnePair, part);
+            part = dot2(q0.w, kOnePair, part);
             if (valid) {
                 // pairs (x_j, x_{j+4}), j = 0..3
                 uint4 q;
-                q.x = (q0.x & 0xffffu) | (q0.z << 16);
-                q.y = (q0.x >> 16) | (q0.z & 0xffff0000u);
-                q.z = (q0.y & 0xffffu) | (q0.w << 16);
-                q.w = (q0.y >> 16) | (q0.w & 0xffff0000u);
+                q.x = __builtin_amdgcn_perm(q0.z, q0.x, 0x05040100u);
+                q.y = __builtin_amdgcn_perm(q0.z, q0.x, 0x07060302u);
+                q.z = __builtin_amdgcn_perm(q0.w, q0.y, 0x05040100u);
+                q.w = __builtin_amdgcn_perm(q0.w, q0.y, 0x07060302u);
                 *reinterpret_cast<uint4*>(dst + lds_phys(l * 16)) = q;
             }
         } else {
+            // sum: v_dot2_f32_bf16 chains of each half's four natural pairs against
+            // (1, 1), from 0; then the two halves added
             const uint32_t dw[8] = {d[0].x, d[0].y, d[0].z, d[0].w, d[1].x, d[1].y, d[1].z, d[1].w};
-            float pa = bf16_bits_to_f32(dw[0] & 0xffffu);
-            pa = pa + bf16_bits_to_f32(dw[0] >> 16);
+            float pa = dot2(dw[0], kOnePair, 0.0f);
+            float pb = dot2(dw[4], kOnePair, 0.0f);
 #pragma unroll
             for (int k = 1; k < 4; ++k) {
-                pa = pa + bf16_bits_to_f32(dw[k] & 0xffffu);
-                pa = pa + bf16_bits_to_f32(dw[k] >> 16);
-            }
-            float pb = bf16_bits_to_f32(dw[4] & 0xffffu);
-            pb = pb + bf16_bits_to_f32(dw[4] >> 16);
-#pragma unroll
-            for (int k = 5; k < 8; ++k) {
-                pb = pb + bf16_bits_to_f32(dw[k] & 0xffffu);
-                pb = pb + bf16_bits_to_f32(dw[k] >> 16);
+                pa = dot2(dw[k], kOnePair, pa);
+                pb = dot2(dw[4 + k], kOnePair, pb);
             }
             part = pa + pb;
             if (valid) {
                 // pairs (x_j, x_{j+8}), j = 0..7
                 uint32_t pr[8];
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const uint32_t lo = (j & 1) ? (dw[j >> 1] >> 16) : (dw[j >> 1] & 0xffffu);
-                    const uint32_t hi = (j & 1) ? (dw[4 + (j >> 1)] & 0xffff0000u) : (dw[4 + (j >> 1)] << 16);
-                    pr[j] = lo | hi;
-                }
+                for (int j = 0; j < 8; ++j)
+                    pr[j] = __builtin_amdgcn_perm(dw[4 + (j >> 1)], dw[j >> 1], (j & 1) ? 0x07060302u : 0x05040100u);
                 *reinterpret_cast<uint4*>(dst + lds_phys(l * 32)) = make_uint4(pr[0], pr[1], pr[2], pr[3]);
                 *reinterpret_cast<uint4*>(dst + lds_phys(l * 32 + 16)) = make_uint4(pr[4], pr[5], pr[6], pr[7]);
             }
@@ -675,7 +672,9 @@ void qmv_affine_kernel(const Params p)
                     const float fs = SBF ? bf16_to_f32_here(sb[s][r]) : f16_to_f32_here(sb[s][r]);
                     const float fb = SBF ? bf16_to_f32_here(bb[s][r]) : f16_to_f32_here(bb[s][r]);
                     sv[r] = own ? fs : 0.0f;
-                    bv[r] = own ? fb : 0.0f;
+                    // bias with the code offset folded in: b' = b - 2^bits s (bf16
+                    // activations; D' then carries the offset, see the fold)
+                    bv[r] = own ? (XF32 ? fb : __builtin_fmaf(-(float)OFFSET, fs, fb)) : 0.0f;
                 }
                 const int gl = c_tw * (kWave / LPG) + gl0;    // group within the window
                 const int xo0 = xl + c_tw * XSTEP;            // chunk's LDS offset (never straddles padding)
@@ -709,7 +708,6 @@ void qmv_affine_kernel(const Params p)
 #pragma unroll
                         for (int i = 0; i < NP; ++i) d = dot2(qp[i], xp[i], d);
                         d = lane_group_sum<LPG>(d);
-                        d = __builtin_fmaf(-(float)OFFSET, S, d);
                         a = pinned(__builtin_fmaf(sv[r], d, __builtin_fmaf(bv[r], S, a)));
                     };
                     if constexpr (M <= R) {
@@ -741,8 +739,7 @@ void qmv_affine_kernel(const Params p)
                             }
 #pragma unroll
                             for (int m = 0; m < M; ++m) {
-                                float dd = lane_group_sum<LPG>(d[m]);
-                                dd = __builtin_fmaf(-(float)OFFSET, S[m], dd);
+                                const float dd = lane_group_sum<LPG>(d[m]);
                                 acc[r][m] = pinned(__builtin_fmaf(sv[r], dd, __builtin_fmaf(bv[r], S[m], acc[r][m])));
                             }
                         }

@@ -13,7 +13,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(PKG, "lib", "libqmv.so")
 
 DT_F32, DT_F16, DT_BF16 = 0, 1, 2
-MAX_M = 13
+MAX_M = 65536     # vectors per call
+TILE_M = 13       # vectors per kernel launch
 
 
 class QmvError(RuntimeError):

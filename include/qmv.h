@@ -78,7 +78,15 @@ enum {
     QMV_E_LAUNCH = 10   /* the HIP runtime refused the launch (e.g. no gfx950 device) */
 };
 
-#define QMV_MAX_M 13
+/* Vectors per call.  One kernel launch serves at most QMV_TILE_M vectors (the
+ * served range of the streamed qmv: mlxcel issue "an order-preserving streamed
+ * qmv would give MTP the fast kernel and byte-identity together", section
+ * "Scope limits"); a call with more runs them as balanced tiles of at most
+ * QMV_TILE_M vectors, launched in order on the stream.  Each vector's arithmetic
+ * is the same in every tile, so every output vector is bit-identical to the
+ * one-vector call on that vector for any M. */
+#define QMV_MAX_M 65536
+#define QMV_TILE_M 13
 /* Largest K (keeps every LDS and row offset inside 32-bit arithmetic). */
 #define QMV_MAX_K (1 << 20)
 #define QMV_MAX_N (1 << 28)
@@ -86,7 +94,7 @@ enum {
 /*
  * y = qmv(x) with the common dtypes: x bf16, scales and biases bf16, y bf16.
  *   w_packed, scales, biases, x, y: device pointers as laid out above.
- *   M in [1, 13]; N >= 1; K >= group_size, K % group_size == 0;
+ *   M in [1, QMV_MAX_M]; N >= 1; K >= group_size, K % group_size == 0;
  *   bits in {2, 4}; group_size in {64, 128}; stream: hipStream_t or NULL.
  * Returns QMV_OK or a QMV_E_* status.
  */

@@ -67,7 +67,7 @@ def call(L, w=W, s=SC, b=BI, x=X, y=Y, **kw):
     (dict(gs=32), 3), (dict(gs=256), 3),
     (dict(N=0), 4), (dict(N=-5), 4), (dict(K=0), 4), (dict(K=96), 4), (dict(K=32), 4),
     (dict(K=(1 << 20) + 64), 4),
-    (dict(M=0), 5), (dict(M=14), 5), (dict(M=-1), 5),
+    (dict(M=0), 5), (dict(M=65537), 5), (dict(M=-1), 5),
     (dict(w=W + 8), 6), (dict(s=SC + 4), 6), (dict(b=BI + 2), 6), (dict(x=X + 8), 6),
     (dict(y=Y + 1), 6), (dict(y=Y + 2, ydt=0), 6),
     (dict(xdt=1), 7), (dict(xdt=5), 7), (dict(sdt=0), 7), (dict(ydt=1), 7),
@@ -82,7 +82,7 @@ def test_kernel_info_validates(L):
     from bit_quantized_gemv_amd import qmv
     info = qmv.KernelInfo()
     assert L.qmv_kernel_info(1, 256, 512, 3, 64, 2, 0, ctypes.byref(info)) == 2
-    assert L.qmv_kernel_info(14, 256, 512, 4, 64, 2, 0, ctypes.byref(info)) == 5
+    assert L.qmv_kernel_info(65537, 256, 512, 4, 64, 2, 0, ctypes.byref(info)) == 5
     assert L.qmv_kernel_info(1, 256, 512, 4, 64, 2, 0, None) == 1
 
 

@@ -77,3 +77,22 @@ def test_error_status_on_gpu():
         q.affine(w, s, b, x[:13], bits=3, group_size=64)
     with pytest.raises(q.QmvError):
         q.affine(w, s, b, x[:5], bits=4, group_size=64, rows_per_wave=3)
+
+
+@pytest.mark.parametrize("name", ["tiny_4b_g64", "up_4b_15360x3840", "up_2b_15360x3840"])
+def test_more_than_one_tile_of_vectors(name):
+    # M beyond one launch's 13 vectors runs as balanced tiles (14 -> 7 + 7,
+    # 27 -> 9 x 3, 40 -> 10 x 4); every vector must still equal its one-vector call
+    p = gen.make_problem(name)
+    dev = U.to_dev(p)
+    xs = gen.make_x(p.K, p.x_dtype, gen.WORKLOADS[name]["seed"], rows=40)
+    xd = U.x_to_dev(xs, p.x_dtype)
+    ones = [U.gpu(p, dev, 1, torch.float32, x=xd[m:m + 1]) for m in range(40)]
+    for M in (14, 27, 40):
+        U.say(f"tiles {name} M={M}")
+        y = U.gpu(p, dev, M, torch.float32, x=xd)
+        assert y.shape[0] == M
+        for m in range(M):
+            assert torch.equal(_bits(y[m]), _bits(ones[m][0])), f"{name}: M={M} vector {m}"
+    if name == "tiny_4b_g64":
+        U.check_parity(U.gpu(p, dev, 40, torch.float32, x=xd), U.ref(p, 40, x=xs), f"{name} M=40")
