@@ -93,12 +93,14 @@ int make_plan(int M, int N, int K, int bits, int gs, bool xf32, bool sbf, int R,
     const int chunks = K * bits / 128;
     const int nsteps = (chunks + qmv::kWave - 1) / qmv::kWave;
     const int xcb = (128 / bits) * (xf32 ? 4 : 2);
-    int ws = nsteps, x_m = 0, s_bytes = 0, total = 0;
+    // per vector and window: padded activations and a float2 per chunk
+    // (dot-chain start, group sum)
+    int ws = nsteps, x_m = 0, sc_bytes = 0, total = 0;
     for (;;) {
         const int logical = ws * qmv::kWave * xcb;
         x_m = logical + logical / 16;
-        s_bytes = M * (ws * qmv::kWave / lpg) * 4;
-        total = M * x_m + s_bytes;
+        sc_bytes = M * ws * qmv::kWave * 8;
+        total = M * x_m + sc_bytes;
         if (total <= qmv::kLdsBytes || ws == 1) break;
         --ws;
     }
@@ -108,7 +110,7 @@ int make_plan(int M, int N, int K, int bits, int gs, bool xf32, bool sbf, int R,
     {
         const int logical = ws * qmv::kWave * xcb;
         x_m = logical + logical / 16;
-        s_bytes = M * (ws * qmv::kWave / lpg) * 4;
+        sc_bytes = M * ws * qmv::kWave * 8;
     }
     Params& p = pl.p;
     p.N = N;
@@ -121,9 +123,8 @@ int make_plan(int M, int N, int K, int bits, int gs, bool xf32, bool sbf, int R,
     p.nwin = nwin;
     p.n_rb = (N + W * R - 1) / (W * R);
     p.x_m_bytes = x_m;
-    p.gw = ws * qmv::kWave / lpg;
     p.s_off = M * x_m;
-    pl.lds = p.s_off + ((s_bytes + 15) / 16) * 16;
+    pl.lds = p.s_off + sc_bytes;
     pl.R = R;
     pl.W = W;
     pl.PF = PF;

@@ -37,10 +37,12 @@
 // never depends on M, R, W, PF, the grid or the K-window size):
 //   1. bf16 activations: the chunk's codes become exact bf16 pairs
 //      (2^bits + q_a, 2^bits + q_b) -- the code sits in the top mantissa bits
-//      of a number in [2^bits, 2^(bits+1)) -- and D'_c is the chain of
-//      v_dot2_f32_bf16 over the chunk's pairs, from 0, in word order then pair
-//      order.  Pair j of a word holds fields (j, j + 32/(2 bits)); the matching
-//      activation pairs are laid out that way in LDS.
+//      of a number in [2^bits, 2^(bits+1)) -- and D_c is the chain of
+//      v_dot2_f32_bf16 over the chunk's pairs in word order then pair order,
+//      starting from -2^bits * S_c (S_c: the chunk's activation sum), so it
+//      ends at the chunk's raw integer dot sum_k q_k x_k.  Pair j of a word
+//      holds fields (j, j + 32/(2 bits)); the matching activation pairs are
+//      laid out that way in LDS.
 //      fp32 activations: D'_c is the fma chain over the chunk's values in
 //      ascending k, from 0, with exact fp32 codes.
 //   2. The lpg = gs*bits/128 chunks of a group sit in adjacent lanes; their
@@ -49,14 +51,14 @@
 //      each 8-value block (16 at 2 bits) is a v_dot2_f32_bf16 chain of its
 //      natural pairs (x_2i, x_2i+1) against (1, 1) from 0 (at 2 bits two
 //      8-value chains, then added); fp32 activations: 8-value blocks summed
-//      left to right.  Blocks are combined pairwise (xor-1, xor-2, ... tree).
+//      left to right.  Blocks are combined pairwise (xor-1, xor-2, ... tree);
+//      the level that completes a chunk gives S_c of step 1.
 //   4. Each group is folded once, by its owner lane (lane % lpg == step % lpg):
-//      acc = fma(scale, D', fma(bias', S, acc)), over its groups in ascending
-//      step, where bias' = fma(-2^bits, scale, bias) for bf16 activations (D'
-//      carries the code offset: scale*D' + bias'*S = scale*D + bias*S in exact
-//      arithmetic) and bias' = bias for fp32 activations.  Every lane executes
-//      the fold; scale and bias are zero on the other lanes, whose
-//      accumulators it leaves unchanged (up to the sign of a zero).
+//      acc = fma(scale, D, fma(bias, S, acc)), over its groups in ascending
+//      step: the scale multiplies the group's raw integer dot D, the bias its
+//      activation sum S.  Every lane executes the fold; scale and bias are zero
+//      on the other lanes, whose accumulators it leaves unchanged (up to the
+//      sign of a zero).
 //   5. Row total: lanes l and l ^ d combined for d = 32, 16, 8, 4, 2, 1 in that
 //      order; then round-to-nearest-even to y's dtype.
 #pragma once
@@ -89,8 +91,9 @@ struct Params {
     int n_rb;            // row blocks of W*R rows
     int y_bf16;          // y: 1 = bf16, 0 = fp32
     int x_m_bytes;       // LDS bytes of one vector's activation window (padded)
-    int gw;              // group sums per vector and window (win_steps * 64 / lpg)
-    int s_off;           // LDS offset of S[M][gw] (fp32)
+    int s_off;           // LDS offset of SC[M][win_steps * 64]: per chunk a float2 (dot-chain
+                         // start -2^bits * chunk sum for bf16 activations, 0 for fp32;
+                         // sum of the chunk's group)
 };
 
 // ------------------------------------------------------------------ helpers
@@ -136,6 +139,18 @@ __device__ __forceinline__ float lane_group_sum(float v)
     if constexpr (NL >= 4) v = v + dpp<kQuadXor2>(v);
     if constexpr (NL >= 8) v = v + dpp<kRowHalfMirror>(v);
     if constexpr (NL >= 16) v = v + dpp<kRowMirror>(v);
+    return v;
+}
+
+// The levels of lane_group_sum<TO> past those of lane_group_sum<FROM>: applied to
+// lane_group_sum<FROM>(v) it gives lane_group_sum<TO>(v) bit for bit.
+template <int FROM, int TO>
+__device__ __forceinline__ float lane_group_sum_from(float v)
+{
+    if constexpr (TO >= 2 && FROM < 2) v = v + dpp<kQuadXor1>(v);
+    if constexpr (TO >= 4 && FROM < 4) v = v + dpp<kQuadXor2>(v);
+    if constexpr (TO >= 8 && FROM < 8) v = v + dpp<kRowHalfMirror>(v);
+    if constexpr (TO >= 16 && FROM < 16) v = v + dpp<kRowMirror>(v);
     return v;
 }
 
@@ -275,6 +290,7 @@ struct Stager {
     static constexpr int XCB = VPC * (XF32 ? 4 : 2);          // LDS bytes per chunk
     static constexpr int UV = (!XF32 && BITS == 2) ? 16 : 8;  // values per unit
     static constexpr int UPG = GS / UV;                       // units per group
+    static constexpr int UPC = VPC / UV;                      // units per chunk
     static constexpr int NLD = (XF32 || BITS == 2) ? 2 : 1;   // 16-byte loads per unit
     static constexpr int XB = ((M <= 2) ? 4 : (M <= 6 ? 8 : 16)) / NLD;  // rounds in flight
 
@@ -311,7 +327,7 @@ struct Stager {
     {
         const int l = j * (int)blockDim.x + (int)threadIdx.x;
         const bool valid = l < upm;
-        float* S = reinterpret_cast<float*>(lds + p.s_off);
+        float2* SC = reinterpret_cast<float2*>(lds + p.s_off);
         uint8_t* dst = lds + m * p.x_m_bytes;
         float part;
         if constexpr (XF32) {
@@ -368,24 +384,30 @@ struct Stager {
         // group sum: the UPG units of a group sit in UPG adjacent lanes (a
         // round starts at a multiple of the wavefront size and a window holds
         // whole groups, so the lanes past the window form whole groups too)
-        part = lane_group_sum<UPG>(part);
-        if (valid && (l % UPG) == 0) S[m * p.gw + l / UPG] = part;
+        // chunk sums (the UPC units of a chunk sit in adjacent lanes), then group
+        // sums (the LPG chunks of a group sit in adjacent lanes, and a window
+        // holds whole groups); each chunk's lane pair stores (start, group sum)
+        float c0 = 0.0f;
+        part = lane_group_sum<UPC>(part);
+        if constexpr (!XF32) c0 = -(float)(1 << BITS) * part;
+        part = lane_group_sum_from<UPC, UPG>(part);
+        if (valid && (l % UPC) == 0) SC[m * p.win_steps * kWave + l / UPC] = make_float2(c0, part);
     }
 
-    // zero the activations and group sums of the window's chunks past the
-    // row's end (only the last window of a row has them)
+    // zero the activations, chain starts and group sums of the window's chunks
+    // past the row's end (only the last window of a row has them)
     __device__ void zero_tail(const Params& p, uint8_t* lds) const
     {
         const int pieces = (p.win_steps * kWave - c_n) * XCB / 16;
-        const int groups = p.gw - c_n / LPG;
-        float* S = reinterpret_cast<float*>(lds + p.s_off);
+        const int cw = p.win_steps * kWave;
+        float2* SC = reinterpret_cast<float2*>(lds + p.s_off);
 #pragma unroll
         for (int m = 0; m < M; ++m) {
             for (int j = (int)threadIdx.x; j < pieces; j += (int)blockDim.x)
                 *reinterpret_cast<uint4*>(lds + m * p.x_m_bytes + lds_phys(c_n * XCB + 16 * j)) =
                     make_uint4(0, 0, 0, 0);
-            for (int j = (int)threadIdx.x; j < groups; j += (int)blockDim.x)
-                S[m * p.gw + c_n / LPG + j] = 0.0f;
+            for (int j = (int)threadIdx.x; j < cw - c_n; j += (int)blockDim.x)
+                SC[m * cw + c_n + j] = make_float2(0.0f, 0.0f);
         }
     }
 
@@ -559,7 +581,8 @@ void qmv_affine_kernel(const Params p)
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
     const int W = blockDim.x / kWave;
     const int grid = gridDim.x;
-    const float* Slds = reinterpret_cast<const float*>(lds + p.s_off);
+    const float2* SClds = reinterpret_cast<const float2*>(lds + p.s_off);
+    const int cwin = p.win_steps * kWave;                  // chunks per window
 
     if ((int)blockIdx.x >= p.n_rb) return;
     const int n_my = (p.n_rb - 1 - (int)blockIdx.x) / grid + 1;   // row blocks of this workgroup
@@ -672,20 +695,23 @@ void qmv_affine_kernel(const Params p)
                     const float fs = SBF ? bf16_to_f32_here(sb[s][r]) : f16_to_f32_here(sb[s][r]);
                     const float fb = SBF ? bf16_to_f32_here(bb[s][r]) : f16_to_f32_here(bb[s][r]);
                     sv[r] = own ? fs : 0.0f;
-                    // bias with the code offset folded in: b' = b - 2^bits s (bf16
-                    // activations; D' then carries the offset, see the fold)
-                    bv[r] = own ? (XF32 ? fb : __builtin_fmaf(-(float)OFFSET, fs, fb)) : 0.0f;
+                    bv[r] = own ? fb : 0.0f;
                 }
                 const int gl = c_tw * (kWave / LPG) + gl0;    // group within the window
                 const int xo0 = xl + c_tw * XSTEP;            // chunk's LDS offset (never straddles padding)
+                const int cl = c_tw * kWave + lane;           // chunk within the window
 
                 if constexpr (!XF32) {
                     // ---- bf16 activations: exact code pairs and v_dot2_f32_bf16
                     constexpr int NP = 64 / BITS;              // code pairs per chunk
                     constexpr int PPW = 16 / BITS;             // pairs per word
-                    auto read_x = [&](int m, int xo, uint32_t (&xp)[NP], float& S) {
+                    // activation pairs of vector m for this lane's chunk, the chunk's
+                    // chain start and the group's sum
+                    auto read_x = [&](int m, int xo, uint32_t (&xp)[NP], float& S, float& c0) {
                         const uint8_t* xs = lds + m * p.x_m_bytes + xo;
-                        S = Slds[m * p.gw + gl];
+                        const float2 sc = SClds[m * cwin + cl];
+                        c0 = sc.x;
+                        S = sc.y;
 #pragma unroll
                         for (int v = 0; v < NP / 4; ++v) {
                             const uint4 t4 = *reinterpret_cast<const uint4*>(xs + v * 16);
@@ -700,11 +726,12 @@ void qmv_affine_kernel(const Params p)
 #pragma unroll
                             for (int j = 0; j < PPW; ++j) qp[i * PPW + j] = code_pair<BITS>(wd[i], j, magic);
                     };
-                    // one vector's chain over a row's pairs, the offset removed, and the
-                    // fold of the group (a no-op on all lanes but the owner)
+                    // one vector's chain over a row's pairs from the chunk's start
+                    // -2^bits*S_chunk (so it ends at the raw integer dot), the group's
+                    // combine, and the fold (a no-op on all lanes but the owner)
                     auto chain_fold = [&](const uint32_t (&qp)[NP], const uint32_t (&xp)[NP], float S,
-                                          int r, float& a) {
-                        float d = 0.0f;
+                                          float c0, int r, float& a) {
+                        float d = c0;
 #pragma unroll
                         for (int i = 0; i < NP; ++i) d = dot2(qp[i], xp[i], d);
                         d = lane_group_sum<LPG>(d);
@@ -717,15 +744,15 @@ void qmv_affine_kernel(const Params p)
                         // order as decoding the whole chunk first; only the pairs of one
                         // word are live at once)
                         uint32_t xp[M][NP];
-                        float S[M];
+                        float S[M], c0[M];
 #pragma unroll
-                        for (int m = 0; m < M; ++m) read_x(m, xo0, xp[m], S[m]);
+                        for (int m = 0; m < M; ++m) read_x(m, xo0, xp[m], S[m], c0[m]);
 #pragma unroll
                         for (int r = 0; r < R; ++r) {
                             const uint32_t wd[4] = {wcur[r].x, wcur[r].y, wcur[r].z, wcur[r].w};
                             float d[M];
 #pragma unroll
-                            for (int m = 0; m < M; ++m) d[m] = 0.0f;
+                            for (int m = 0; m < M; ++m) d[m] = c0[m];
 #pragma unroll
                             for (int i = 0; i < 4; ++i) {
                                 uint32_t qw[PPW];
@@ -749,8 +776,8 @@ void qmv_affine_kernel(const Params p)
                         // read is tied to vector m-1's last result, so the compiler
                         // cannot hoist every vector's reads (and registers) up front.
                         uint32_t xq[2][NP];
-                        float Sq[2];
-                        read_x(0, xo0, xq[0], Sq[0]);
+                        float Sq[2], cq[2];
+                        read_x(0, xo0, xq[0], Sq[0], cq[0]);
                         uint32_t qp[R][NP];
 #pragma unroll
                         for (int r = 0; r < R; ++r) decode(wcur[r], qp[r]);
@@ -758,10 +785,10 @@ void qmv_affine_kernel(const Params p)
                         for (int m = 0; m < M; ++m) {
                             if (m + 1 < M) {
                                 const int xo = (m == 0) ? xo0 : after(xo0, acc[R - 1][m - 1]);
-                                read_x(m + 1, xo, xq[(m + 1) & 1], Sq[(m + 1) & 1]);
+                                read_x(m + 1, xo, xq[(m + 1) & 1], Sq[(m + 1) & 1], cq[(m + 1) & 1]);
                             }
 #pragma unroll
-                            for (int r = 0; r < R; ++r) chain_fold(qp[r], xq[m & 1], Sq[m & 1], r, acc[r][m]);
+                            for (int r = 0; r < R; ++r) chain_fold(qp[r], xq[m & 1], Sq[m & 1], cq[m & 1], r, acc[r][m]);
                             // keep each vector's folds next to its chains (left free, the
                             // scheduler sinks them and holds every chain result live)
                             __builtin_amdgcn_sched_barrier(0);
@@ -816,7 +843,7 @@ void qmv_affine_kernel(const Params p)
                     }
 #pragma unroll
                     for (int m = 0; m < M; ++m) {
-                        const float S = Slds[m * p.gw + gl];
+                        const float S = SClds[m * cwin + cl].y;
 #pragma unroll
                         for (int r = 0; r < R; ++r) {
                             const float d = lane_group_sum<LPG>(dsum[r][m]);
