@@ -2,6 +2,7 @@
 through the C ABI, and the oracle comparison of the parity bar."""
 from __future__ import annotations
 
+import os
 import sys
 
 import numpy as np
@@ -75,6 +76,10 @@ def check_parity(got: torch.Tensor, want: np.ndarray, what: str, tol: float = TO
         worst = max(worst, rel)
         assert np.all(np.isfinite(g[m])), f"{what}: non-finite output in vector {m}"
         assert rel <= tol, f"{what}: vector {m} normwise error {rel:.3e} > {tol:g}"
+    log = os.environ.get("QMV_PARITY_LOG")
+    if log:                          # optional record of the errors seen, one line per check
+        with open(log, "a") as f:
+            f.write(f"{what}\t{worst:.3e}\n")
     return worst
 
 
