@@ -221,8 +221,10 @@ int try_plan(int M, int N, int K, int bits, int gs, bool xf32, bool sbf, int R, 
 //   * M >= 3, bound by the vector ALUs: 8 wavefronts, one unit in flight, and
 //     the R that minimises the rows the busiest compute unit processes,
 //     weighted by the per-row cost of fewer rows per wavefront (the
-//     activations read from LDS and the decode are shared by fewer rows): 1.5x
-//     for two rows and 2.5x for one row, relative to four.
+//     activations read from LDS and the decode are shared by fewer rows): 1.1x
+//     for two rows and 2.5x for one row, relative to four (one row per
+//     wavefront reads the activations from LDS once per row, which makes it
+//     LDS-bound where the vector ALUs are busy).
 //   * 2-bit codes have no four-row instances; K-windowed calls have one unit
 //     in flight.
 int choose_plan(int M, int N, int K, int bits, int gs, bool xf32, bool sbf, int R_req, Plan& best)
@@ -250,7 +252,7 @@ int choose_plan(int M, int N, int K, int bits, int gs, bool xf32, bool sbf, int 
             }
     } else {
         const int Rs[3] = {4, 2, 1};
-        const double cost[3] = {1.0, 1.5, 2.5};
+        const double cost[3] = {1.0, 1.1, 2.5};
         double best_score = 0.0;
         bool found = false;
         for (int i = 0; i < 3; ++i) {
@@ -296,6 +298,29 @@ int vectors_per_launch(int M, int N, int K, int bits, int gs, bool xf32)
     return (M + tiles - 1) / tiles;
 }
 
+// Vectors per launch, final: when a launch of vectors_per_launch() vectors
+// would window K (its activations do not fit in LDS whole) and its workgroups
+// walk more than one row block each, every block restages every window.  If
+// tiles of at least half as many vectors fit whole K, the vectors are cut
+// into those instead (measured on the 17408 x 5120 projection at M = 13:
+// two whole-K launches take ~20% less time than one windowed launch).
+int tile_vectors(int M, int N, int K, int bits, int gs, bool xf32, bool sbf, int R_req)
+{
+    const int mc = vectors_per_launch(M, N, K, bits, gs, xf32);
+    if (mc < 2) return mc;
+    Plan pl;
+    if (choose_plan(mc, N, K, bits, gs, xf32, sbf, R_req, pl) != QMV_OK) return mc;
+    if (pl.p.nwin == 1 || pl.p.n_rb <= pl.grid) return mc;
+    for (int mk = mc - 1; mk >= (mc + 1) / 2; --mk) {
+        Plan q;
+        if (make_plan(mk, N, K, bits, gs, xf32, sbf, 1, 1, 1, q) == QMV_OK && q.p.nwin == 1) {
+            const int tiles = (M + mk - 1) / mk;
+            return (M + tiles - 1) / tiles;
+        }
+    }
+    return mc;
+}
+
 }  // namespace
 
 extern "C" {
@@ -310,7 +335,7 @@ int qmv_affine_ex(const uint32_t* w_packed, const void* scales, const void* bias
     if (st != QMV_OK) return st;
     const bool xf32 = (x_dt == QMV_DT_F32);
     const bool sbf = (sb_dt == QMV_DT_BF16);
-    const int mc = vectors_per_launch(M, N, K, bits, group_size, xf32);
+    const int mc = tile_vectors(M, N, K, bits, group_size, xf32, sbf, rows_per_wave);
     if (mc < 1) return QMV_E_SHAPE;
     for (int m0 = 0; m0 < M; m0 += mc) {
         const int mm = std::min(mc, M - m0);
@@ -353,7 +378,7 @@ int qmv_kernel_info(int M, int N, int K, int bits, int group_size, qmv_dtype x_d
                         QMV_DT_BF16, QMV_DT_F32, rows_per_wave);
     if (st != QMV_OK) return st;
     const bool xf32 = (x_dt == QMV_DT_F32);
-    const int mc = vectors_per_launch(M, N, K, bits, group_size, xf32);
+    const int mc = tile_vectors(M, N, K, bits, group_size, xf32, true, rows_per_wave);
     if (mc < 1) return QMV_E_SHAPE;
     Plan pl;
     st = choose_plan(mc, N, K, bits, group_size, xf32, true, rows_per_wave, pl);

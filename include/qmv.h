@@ -82,9 +82,10 @@ enum {
  * served range of the streamed qmv: mlxcel issue "an order-preserving streamed
  * qmv would give MTP the fast kernel and byte-identity together", section
  * "Scope limits"); a call with more runs them as balanced tiles of at most
- * QMV_TILE_M vectors, launched in order on the stream.  Each vector's arithmetic
- * is the same in every tile, so every output vector is bit-identical to the
- * one-vector call on that vector for any M. */
+ * QMV_TILE_M vectors, launched in order on the stream.  Fewer vectors per tile
+ * are used where the activations of QMV_TILE_M vectors do not fit in LDS whole
+ * (long K).  Each vector's arithmetic is the same in every tile, so every output
+ * vector is bit-identical to the one-vector call on that vector for any M. */
 #define QMV_MAX_M 65536
 #define QMV_TILE_M 13
 /* Largest K (keeps every LDS and row offset inside 32-bit arithmetic). */
@@ -117,7 +118,8 @@ int qmv_affine_ex(const uint32_t* w_packed, const void* scales, const void* bias
                   void* stream);
 
 /* Resources and launch shape of the kernel the library would use for a call
- * with these arguments (no launch is made; needs a gfx950 device for the
+ * with these arguments (its first launch, when the call is cut into several
+ * tiles of vectors; no launch is made; needs a gfx950 device for the
  * occupancy query).  Fields: vgprs (architected VGPRs per lane as compiled),
  * scratch_bytes (private memory per lane; 0 = no register spills), lds_bytes
  * per workgroup (dynamic), wg_size (threads), grid (workgroups),
