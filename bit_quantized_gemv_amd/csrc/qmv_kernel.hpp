@@ -776,8 +776,19 @@ void qmv_affine_kernel(const Params p)
                         // read is tied to vector m-1's last result, so the compiler
                         // cannot hoist every vector's reads (and registers) up front.
                         uint32_t xq[2][NP];
-                        float Sq[2], cq[2];
-                        read_x(0, xo0, xq[0], Sq[0], cq[0]);
+                        float Sq[2], cq[2][R];
+                        // Every row's chain needs the start in a register of its own (the
+                        // dot2 accumulates in place); reading it once per row from LDS
+                        // (volatile, so the reads are not merged) spares a vector-ALU
+                        // copy per row and vector.
+                        auto read_xr = [&](int m, int xo, uint32_t (&xp)[NP], float& S, float (&c0)[R]) {
+                            read_x(m, xo, xp, S, c0[0]);
+                            typedef __attribute__((address_space(3))) const volatile float lds_f32;
+                            lds_f32* cs = (lds_f32*)(&SClds[m * cwin + cl].x);
+#pragma unroll
+                            for (int r = 1; r < R; ++r) c0[r] = *cs;
+                        };
+                        read_xr(0, xo0, xq[0], Sq[0], cq[0]);
                         uint32_t qp[R][NP];
 #pragma unroll
                         for (int r = 0; r < R; ++r) decode(wcur[r], qp[r]);
@@ -785,10 +796,10 @@ void qmv_affine_kernel(const Params p)
                         for (int m = 0; m < M; ++m) {
                             if (m + 1 < M) {
                                 const int xo = (m == 0) ? xo0 : after(xo0, acc[R - 1][m - 1]);
-                                read_x(m + 1, xo, xq[(m + 1) & 1], Sq[(m + 1) & 1], cq[(m + 1) & 1]);
+                                read_xr(m + 1, xo, xq[(m + 1) & 1], Sq[(m + 1) & 1], cq[(m + 1) & 1]);
                             }
 #pragma unroll
-                            for (int r = 0; r < R; ++r) chain_fold(qp[r], xq[m & 1], Sq[m & 1], cq[m & 1], r, acc[r][m]);
+                            for (int r = 0; r < R; ++r) chain_fold(qp[r], xq[m & 1], Sq[m & 1], cq[m & 1][r], r, acc[r][m]);
                             // keep each vector's folds next to its chains (left free, the
                             // scheduler sinks them and holds every chain result live)
                             __builtin_amdgcn_sched_barrier(0);
