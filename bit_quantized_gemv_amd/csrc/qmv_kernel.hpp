@@ -53,14 +53,21 @@
 //      8-value chains, then added); fp32 activations: 8-value blocks summed
 //      left to right.  Blocks are combined pairwise (xor-1, xor-2, ... tree);
 //      the level that completes a chunk gives S_c of step 1.
-//   4. Each group is folded once, by its owner lane (lane % lpg == step % lpg):
+//   4. Each group is folded once, by its owner lane -- for row n, the lane l
+//      of the group with l % lpg == n % lpg -- as
 //      acc = fma(scale, D, fma(bias, S, acc)), over its groups in ascending
 //      step: the scale multiplies the group's raw integer dot D, the bias its
-//      activation sum S.  Every lane executes the fold; scale and bias are zero
-//      on the other lanes, whose accumulators it leaves unchanged (up to the
-//      sign of a zero).
+//      activation sum S.  With lpg = 2 and an even number of rows per
+//      wavefront (and more than one vector), the two lanes of a group run the
+//      chains of both rows of a pair with the rows swapped on the odd lane, so
+//      one DPP add leaves each lane the group dot of its own row (the same two
+//      addends as step 2) and each lane folds only its own rows.  Otherwise
+//      every lane executes the fold of every row, with scale and bias zeroed
+//      on lanes that do not own the group, which leaves their accumulators at
+//      +0.
 //   5. Row total: lanes l and l ^ d combined for d = 32, 16, 8, 4, 2, 1 in that
-//      order; then round-to-nearest-even to y's dtype.
+//      order (lanes that own none of the row's groups contribute +0); then
+//      round-to-nearest-even to y's dtype.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -481,10 +488,11 @@ constexpr int pow2_at_least(int v) { return v <= 1 ? 1 : 2 * pow2_at_least((v + 
 // keeps a different value than lane l ^ d; once one value remains, the level
 // is a butterfly.  On return, v[0] of lane l holds the total of value
 // reduce_index<P>(l); lanes l with l % (64/P) == 0 hold distinct values.
-template <int P>
+template <int P, bool PAIRS = false>
 __device__ __forceinline__ void lane_reduce(float (&v)[P], int lane)
 {
     static_assert(P >= 1 && P <= 64 && (P & (P - 1)) == 0, "P must be a power of two <= 64");
+    static_assert(!PAIRS || P <= 32, "paired reductions hold at most 32 values");
     // d = 32
     if constexpr (P >= 2) {
 #pragma unroll
@@ -526,16 +534,24 @@ __device__ __forceinline__ void lane_reduce(float (&v)[P], int lane)
     level(std::integral_constant<int, 8>{}, std::integral_constant<int, (P >= 8 ? P / 4 : 1)>{});
     level(std::integral_constant<int, 4>{}, std::integral_constant<int, (P >= 16 ? P / 8 : 1)>{});
     level(std::integral_constant<int, 2>{}, std::integral_constant<int, (P >= 32 ? P / 16 : 1)>{});
-    level(std::integral_constant<int, 1>{}, std::integral_constant<int, (P >= 64 ? P / 32 : 1)>{});
+    if constexpr (!PAIRS) {
+        level(std::integral_constant<int, 1>{}, std::integral_constant<int, (P >= 64 ? P / 32 : 1)>{});
+    } else {
+        // Lanes l and l ^ 1 hold different rows: the xor-1 level of a row's tree
+        // pairs each owner lane with a lane whose partial for that row is +0
+        // (it owns none of the row's groups), which leaves the value unchanged
+        // except that -0 becomes +0.
+        v[0] = v[0] + 0.0f;
+    }
 }
 
-// Which value lane l holds after lane_reduce<P>.
-template <int P>
+// Which value lane l holds after lane_reduce<P, PAIRS>.
+template <int P, bool PAIRS = false>
 __device__ __forceinline__ int reduce_index(int lane)
 {
     int idx = 0, n = P;
 #pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) {
+    for (int d = 32; d >= (PAIRS ? 2 : 1); d >>= 1) {
         if (n >= 2) {
             if (lane & d) idx += n / 2;
             n /= 2;
@@ -570,9 +586,19 @@ void qmv_affine_kernel(const Params p)
     constexpr int XSTEP = kWave * XCB + kWave * XCB / 16;  // padded LDS bytes per wave step
     constexpr int OFFSET = 1 << BITS;             // code offset of the bf16 pairs
     constexpr int NS = PF + 1;                    // ring slots
-    constexpr int V = R * M;
+    // Paired rows: with two lanes per group and an even number of rows, lane
+    // parity selects the row a lane folds -- even lanes own the groups of rows
+    // 2k, odd lanes those of rows 2k + 1 -- so each lane loads the metadata of
+    // R/2 rows, and one combine and one fold serve two rows.  (Every instance
+    // uses this ownership; unpaired ones zero the scale and bias of the rows a
+    // lane does not own, which gives the same bits.  One vector keeps the
+    // unpaired form: its short compute after the last load is latency-bound,
+    // and pairing adds the per-word lane selects to it.)
+    constexpr bool PAIRED = !XF32 && LPG == 2 && (R % 2 == 0) && M >= 2;
+    constexpr int RS = PAIRED ? R / 2 : R;        // rows each lane folds (accumulator sets)
+    constexpr int V = RS * M;
     constexpr int P = pow2_at_least(V);
-    static_assert(P <= 64, "R*M must not exceed 64");
+    static_assert(P <= (PAIRED ? 32 : 64), "too many row totals per lane");
 
     extern __shared__ __align__(16) uint8_t lds[];
     const int lane = threadIdx.x & (kWave - 1);
@@ -601,6 +627,7 @@ void qmv_affine_kernel(const Params p)
     const int row_step = grid * W * R;
     __amdgpu_buffer_rsrc_t i_wr, i_sr, i_br;
     int i_sw[R], i_ss[R];                            // per-row scalar offsets (weights, scales/biases)
+    int i_ps[RS];                                    // paired: offset of the lane's own row of each pair
     auto set_block = [&]() {
         // every input of the resources is wave-uniform; readfirstlane makes that
         // explicit (a resource the compiler cannot prove uniform costs a
@@ -616,20 +643,30 @@ void qmv_affine_kernel(const Params p)
             i_sw[r] = rr * p.row_bytes;
             i_ss[r] = rr * p.G * 2;
         }
+        if constexpr (PAIRED) {
+#pragma unroll
+            for (int k = 0; k < RS; ++k) i_ps[k] = i_ss[2 * k] + (lane & 1) * (i_ss[2 * k + 1] - i_ss[2 * k]);
+        }
     };
     set_block();
     const int wo0 = lane * 16;                       // lane's chunk offset in a row's first step
     const int mo0 = (lane / LPG) * 2;                // lane's group offset in a row's first step
     int i_wo = wo0, i_mo = mo0;
     const int wo_max = p.row_bytes - 16, mo_max = p.G * 2 - 2;
-    auto issue = [&](uint4 (&wv)[R], unsigned short (&sv)[R], unsigned short (&bv)[R]) {
+    auto issue = [&](uint4 (&wv)[R], unsigned short (&sv)[RS], unsigned short (&bv)[RS]) {
         const int wo = min(i_wo, wo_max);
         const int mo = min(i_mo, mo_max);
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            wv[r] = buf_load_nt(i_wr, wo, i_sw[r]);
-            sv[r] = buf_load_u16(i_sr, mo, i_ss[r]);
-            bv[r] = buf_load_u16(i_br, mo, i_ss[r]);
+        for (int r = 0; r < R; ++r) wv[r] = buf_load_nt(i_wr, wo, i_sw[r]);
+#pragma unroll
+        for (int k = 0; k < RS; ++k) {
+            if constexpr (PAIRED) {
+                sv[k] = buf_load_u16(i_sr, mo + i_ps[k], 0);
+                bv[k] = buf_load_u16(i_br, mo + i_ps[k], 0);
+            } else {
+                sv[k] = buf_load_u16(i_sr, mo, i_ss[k]);
+                bv[k] = buf_load_u16(i_br, mo, i_ss[k]);
+            }
         }
         if (++is_t == p.nsteps) {
             is_t = 0;
@@ -647,7 +684,7 @@ void qmv_affine_kernel(const Params p)
     const uint32_t magic = opaque_u32(code_magic<BITS>());
     Stager<BITS, GS, M, XF32> stg;
     uint4 wb[NS][R];
-    unsigned short sb[NS][R], bb[NS][R];    // scale and bias bits
+    unsigned short sb[NS][RS], bb[NS][RS];  // scale and bias bits (of the lane's own rows when paired)
     auto prologue = [&]() {
 #pragma unroll
         for (int s = 0; s < PF; ++s) issue(wb[s], sb[s], bb[s]);
@@ -656,9 +693,9 @@ void qmv_affine_kernel(const Params p)
     stg.stage(p, xr, lds, 0, prologue);
     __syncthreads();
 
-    float acc[R][M];
+    float acc[RS][M];
 #pragma unroll
-    for (int r = 0; r < R; ++r)
+    for (int r = 0; r < RS; ++r)
 #pragma unroll
         for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
     int c_rb = 0, c_t = 0, c_tw = 0, c_win = 0;   // unit consumed next; its step within the window
@@ -685,17 +722,26 @@ void qmv_affine_kernel(const Params p)
                     }
                 }
                 const uint4 (&wcur)[R] = wb[s];
-                // scale and bias of each row's group: zero on every lane but the
-                // group's owner, so the fold acc = s*D + (b*S + acc) leaves a
-                // non-owner's accumulator unchanged without a branch
-                const bool own = (lane % LPG) == (t % LPG);
-                float sv[R], bv[R];
+                // Scale and bias of each row's group.  The group's owner is the lane
+                // l with l % lpg == n % lpg for row n.  Unpaired, every lane folds
+                // every row with the scale and bias zeroed on all lanes but the
+                // owner, so the fold acc = s*D + (b*S + acc) leaves a non-owner's
+                // accumulator unchanged without a branch; paired, each lane loaded
+                // only its own rows' values.
+                const int rb0 = (((int)blockIdx.x + c_rb * grid) * W + wave) * R;   // block's first row
+                float sv[RS], bv[RS];
 #pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    const float fs = SBF ? bf16_to_f32_here(sb[s][r]) : f16_to_f32_here(sb[s][r]);
-                    const float fb = SBF ? bf16_to_f32_here(bb[s][r]) : f16_to_f32_here(bb[s][r]);
-                    sv[r] = own ? fs : 0.0f;
-                    bv[r] = own ? fb : 0.0f;
+                for (int k = 0; k < RS; ++k) {
+                    const float fs = SBF ? bf16_to_f32_here(sb[s][k]) : f16_to_f32_here(sb[s][k]);
+                    const float fb = SBF ? bf16_to_f32_here(bb[s][k]) : f16_to_f32_here(bb[s][k]);
+                    if constexpr (PAIRED) {
+                        sv[k] = fs;
+                        bv[k] = fb;
+                    } else {
+                        const bool own = (lane % LPG) == ((rb0 + k) % LPG);
+                        sv[k] = own ? fs : 0.0f;
+                        bv[k] = own ? fb : 0.0f;
+                    }
                 }
                 const int gl = c_tw * (kWave / LPG) + gl0;    // group within the window
                 const int xo0 = xl + c_tw * XSTEP;            // chunk's LDS offset (never straddles padding)
@@ -712,6 +758,9 @@ void qmv_affine_kernel(const Params p)
                         const float2 sc = SClds[m * cwin + cl];
                         c0 = sc.x;
                         S = sc.y;
+                        // the chain start is needed first: keep its read ahead of the
+                        // activation reads, so the chain can begin as they arrive
+                        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                         for (int v = 0; v < NP / 4; ++v) {
                             const uint4 t4 = *reinterpret_cast<const uint4*>(xs + v * 16);
@@ -747,27 +796,70 @@ void qmv_affine_kernel(const Params p)
                         float S[M], c0[M];
 #pragma unroll
                         for (int m = 0; m < M; ++m) read_x(m, xo0, xp[m], S[m], c0[m]);
+                        if constexpr (PAIRED) {
+                            // rows 2k and 2k+1: an even lane runs chain X over row 2k's
+                            // chunk and chain Y over row 2k+1's, an odd lane the other way
+                            // round; X plus the partner lane's Y is then the group's dot of
+                            // the lane's own row
+                            const bool odd = (lane & 1) != 0;
 #pragma unroll
-                        for (int r = 0; r < R; ++r) {
-                            const uint32_t wd[4] = {wcur[r].x, wcur[r].y, wcur[r].z, wcur[r].w};
-                            float d[M];
+                            for (int k = 0; k < RS; ++k) {
+                                const uint32_t w0[4] = {wcur[2 * k].x, wcur[2 * k].y, wcur[2 * k].z, wcur[2 * k].w};
+                                const uint32_t w1[4] = {wcur[2 * k + 1].x, wcur[2 * k + 1].y, wcur[2 * k + 1].z, wcur[2 * k + 1].w};
+                                float dx[M], dy[M];
 #pragma unroll
-                            for (int m = 0; m < M; ++m) d[m] = c0[m];
+                                for (int m = 0; m < M; ++m) {
+                                    dx[m] = c0[m];
+                                    dy[m] = c0[m];
+                                }
 #pragma unroll
-                            for (int i = 0; i < 4; ++i) {
-                                uint32_t qw[PPW];
+                                for (int i = 0; i < 4; ++i) {
+                                    const uint32_t wa = odd ? w1[i] : w0[i];
+                                    const uint32_t wb2 = odd ? w0[i] : w1[i];
+                                    uint32_t qa[PPW], qb[PPW];
 #pragma unroll
-                                for (int j = 0; j < PPW; ++j) qw[j] = code_pair<BITS>(wd[i], j, magic);
+                                    for (int j = 0; j < PPW; ++j) {
+                                        qa[j] = code_pair<BITS>(wa, j, magic);
+                                        qb[j] = code_pair<BITS>(wb2, j, magic);
+                                    }
 #pragma unroll
-                                for (int m = 0; m < M; ++m)
+                                    for (int m = 0; m < M; ++m)
 #pragma unroll
-                                    for (int j = 0; j < PPW; ++j) d[m] = dot2(qw[j], xp[m][i * PPW + j], d[m]);
-                                __builtin_amdgcn_sched_barrier(0);
+                                        for (int j = 0; j < PPW; ++j) {
+                                            dx[m] = dot2(qa[j], xp[m][i * PPW + j], dx[m]);
+                                            dy[m] = dot2(qb[j], xp[m][i * PPW + j], dy[m]);
+                                        }
+                                    __builtin_amdgcn_sched_barrier(0);
+                                }
+#pragma unroll
+                                for (int m = 0; m < M; ++m) {
+                                    const float dd = dx[m] + dpp<kQuadXor1>(dy[m]);
+                                    acc[k][m] = pinned(__builtin_fmaf(sv[k], dd, __builtin_fmaf(bv[k], S[m], acc[k][m])));
+                                }
                             }
-#pragma unroll
-                            for (int m = 0; m < M; ++m) {
-                                const float dd = lane_group_sum<LPG>(d[m]);
-                                acc[r][m] = pinned(__builtin_fmaf(sv[r], dd, __builtin_fmaf(bv[r], S[m], acc[r][m])));
+                        } else {
+    #pragma unroll
+                            for (int r = 0; r < R; ++r) {
+                                const uint32_t wd[4] = {wcur[r].x, wcur[r].y, wcur[r].z, wcur[r].w};
+                                float d[M];
+    #pragma unroll
+                                for (int m = 0; m < M; ++m) d[m] = c0[m];
+    #pragma unroll
+                                for (int i = 0; i < 4; ++i) {
+                                    uint32_t qw[PPW];
+    #pragma unroll
+                                    for (int j = 0; j < PPW; ++j) qw[j] = code_pair<BITS>(wd[i], j, magic);
+    #pragma unroll
+                                    for (int m = 0; m < M; ++m)
+    #pragma unroll
+                                        for (int j = 0; j < PPW; ++j) d[m] = dot2(qw[j], xp[m][i * PPW + j], d[m]);
+                                    __builtin_amdgcn_sched_barrier(0);
+                                }
+    #pragma unroll
+                                for (int m = 0; m < M; ++m) {
+                                    const float dd = lane_group_sum<LPG>(d[m]);
+                                    acc[r][m] = pinned(__builtin_fmaf(sv[r], dd, __builtin_fmaf(bv[r], S[m], acc[r][m])));
+                                }
                             }
                         }
                     } else {
@@ -790,16 +882,47 @@ void qmv_affine_kernel(const Params p)
                         };
                         read_xr(0, xo0, xq[0], Sq[0], cq[0]);
                         uint32_t qp[R][NP];
+                        if constexpr (PAIRED) {
+                            // chain registers 2k / 2k+1 hold rows 2k / 2k+1 on even lanes
+                            // and rows 2k+1 / 2k on odd lanes (see the few-vector path)
+                            const bool odd = (lane & 1) != 0;
 #pragma unroll
-                        for (int r = 0; r < R; ++r) decode(wcur[r], qp[r]);
+                            for (int k = 0; k < RS; ++k) {
+                                const uint4 w0 = wcur[2 * k], w1 = wcur[2 * k + 1];
+                                const uint4 wa = make_uint4(odd ? w1.x : w0.x, odd ? w1.y : w0.y,
+                                                            odd ? w1.z : w0.z, odd ? w1.w : w0.w);
+                                const uint4 wb2 = make_uint4(odd ? w0.x : w1.x, odd ? w0.y : w1.y,
+                                                             odd ? w0.z : w1.z, odd ? w0.w : w1.w);
+                                decode(wa, qp[2 * k]);
+                                decode(wb2, qp[2 * k + 1]);
+                            }
+                        } else {
+#pragma unroll
+                            for (int r = 0; r < R; ++r) decode(wcur[r], qp[r]);
+                        }
 #pragma unroll
                         for (int m = 0; m < M; ++m) {
                             if (m + 1 < M) {
-                                const int xo = (m == 0) ? xo0 : after(xo0, acc[R - 1][m - 1]);
+                                const int xo = (m == 0) ? xo0 : after(xo0, acc[RS - 1][m - 1]);
                                 read_xr(m + 1, xo, xq[(m + 1) & 1], Sq[(m + 1) & 1], cq[(m + 1) & 1]);
                             }
+                            if constexpr (PAIRED) {
+                                float d[R];
 #pragma unroll
-                            for (int r = 0; r < R; ++r) chain_fold(qp[r], xq[m & 1], Sq[m & 1], cq[m & 1][r], r, acc[r][m]);
+                                for (int r = 0; r < R; ++r) {
+                                    d[r] = cq[m & 1][r];
+#pragma unroll
+                                    for (int i = 0; i < NP; ++i) d[r] = dot2(qp[r][i], xq[m & 1][i], d[r]);
+                                }
+#pragma unroll
+                                for (int k = 0; k < RS; ++k) {
+                                    const float dd = d[2 * k] + dpp<kQuadXor1>(d[2 * k + 1]);
+                                    acc[k][m] = pinned(__builtin_fmaf(sv[k], dd, __builtin_fmaf(bv[k], Sq[m & 1], acc[k][m])));
+                                }
+                            } else {
+#pragma unroll
+                                for (int r = 0; r < R; ++r) chain_fold(qp[r], xq[m & 1], Sq[m & 1], cq[m & 1][r], r, acc[r][m]);
+                            }
                             // keep each vector's folds next to its chains (left free, the
                             // scheduler sinks them and holds every chain result live)
                             __builtin_amdgcn_sched_barrier(0);
@@ -868,19 +991,20 @@ void qmv_affine_kernel(const Params p)
                     float v[P];
 #pragma unroll
                     for (int i = 0; i < P; ++i) v[i] = (i < V) ? acc[i / M][i % M] : 0.0f;
-                    lane_reduce<P>(v, lane);
-                    const int idx = reduce_index<P>(lane);
-                    const int row0 = (((int)blockIdx.x + c_rb * grid) * W + wave) * R;
-                    const int r = idx / M, m = idx - (idx / M) * M;
-                    if ((lane % (64 / P)) == 0 && idx < V && row0 + r < p.N) {
-                        const size_t o = (size_t)m * p.N + row0 + r;
+                    lane_reduce<P, PAIRED>(v, lane);
+                    const int idx = reduce_index<P, PAIRED>(lane);
+                    const int k = idx / M, m = idx - (idx / M) * M;
+                    const int r = PAIRED ? 2 * k + (lane & 1) : k;
+                    const bool holder = PAIRED ? ((lane >> 1) % (32 / P)) == 0 : (lane % (64 / P)) == 0;
+                    if (holder && idx < V && rb0 + r < p.N) {
+                        const size_t o = (size_t)m * p.N + rb0 + r;
                         if (p.y_bf16)
                             static_cast<uint16_t*>(p.y)[o] = (uint16_t)f32_to_bf16_rne(v[0]);
                         else
                             static_cast<float*>(p.y)[o] = v[0];
                     }
 #pragma unroll
-                    for (int rr = 0; rr < R; ++rr)
+                    for (int rr = 0; rr < RS; ++rr)
 #pragma unroll
                         for (int mm = 0; mm < M; ++mm) acc[rr][mm] = 0.0f;
                     c_t = 0;
