@@ -96,3 +96,20 @@ def test_more_than_one_tile_of_vectors(name):
             assert torch.equal(_bits(y[m]), _bits(ones[m][0])), f"{name}: M={M} vector {m}"
     if name == "tiny_4b_g64":
         U.check_parity(U.gpu(p, dev, 40, torch.float32, x=xd), U.ref(p, 40, x=xs), f"{name} M=40")
+
+
+def test_long_k_vectors_cut_into_whole_k_tiles():
+    # 13 vectors of K = 5120 do not fit LDS whole; with 17408 rows each
+    # workgroup walks several row blocks, so the call runs as two whole-K
+    # launches (7 + 6 vectors) instead of one K-windowed launch
+    assert U.q.kernel_info(13, 17408, 5120, 4, 64)["k_windows"] == 1
+    # few rows: one row block per workgroup, so windowing is kept
+    assert U.q.kernel_info(13, 256, 5120, 4, 64)["k_windows"] > 1
+    # vectors still equal their one-vector calls through the tiled launches
+    p = gen.make_problem("up_4b_17408x5120")
+    dev = U.to_dev(p)
+    U.say("whole-K tiles up_4b_17408x5120 M=13")
+    y = U.gpu(p, dev, 13, torch.float32)
+    for m in (0, 6, 7, 12):
+        one = U.gpu(p, dev, 1, torch.float32, x=dev[3][m:m + 1])
+        assert torch.equal(_bits(y[m]), _bits(one[0])), f"vector {m}"
