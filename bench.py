@@ -18,9 +18,15 @@ outputs, each counted once:
     N*K*bits/8 + 2 * N*(K/gs)*2 + M*K*2 + M*N*2.
 
 Prints one JSON line (the driver's contract) with extra objects:
-    roofline      -- the dominant kernel against the HBM peak
-    m13           -- the same matrix at M = 13
-    cpu_baseline  -- the CPU oracle on the machine's host cores (bounded sample)
+    roofline        -- the dominant kernel against the HBM peak
+    stream_ceiling  -- a load-and-discard kernel of the M = 1 launch shape over
+                       the same byte count, with the same rotation: the share of
+                       the peak any one-launch kernel of this size reaches
+    m13             -- the same matrix at M = 13
+    occupancy_17408x5120 -- resources per rows-per-wavefront on the 27B-class
+                       up-projection (no launch)
+    cpu_baseline    -- the CPU oracle on the machine's host cores (bounded sample),
+                       and one of its calls on a single thread
 """
 from __future__ import annotations
 
@@ -130,10 +136,19 @@ def cpu_baseline(p, budget_s: float):
         orc.qmv(p.w_packed, p.scales, p.biases, p.x[:1], bits=p.bits, group_size=p.gs,
                 sb_dtype=oracle.BF16, x_dtype=oracle.BF16, nthreads=cores)
     dt = (time.perf_counter() - t0) / reps
+    one = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        orc.qmv(p.w_packed, p.scales, p.biases, p.x[:1], bits=p.bits, group_size=p.gs,
+                sb_dtype=oracle.BF16, x_dtype=oracle.BF16, nthreads=1)
+        one.append(time.perf_counter() - t0)
+    one.sort()
     return {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": cores,
             "kind": "oracle", "us_per_call": round(dt * 1e6, 1),
             "sample": f"{reps} whole M=1 calls of {p.N}x{p.K} 4-bit g64 (fp64 accumulate, "
                       f"OpenMP over rows), after 1 warm-up call",
+            "us_per_call_1thread": round(one[1] * 1e6, 1),
+            "sample_1thread": "median of 3 whole M=1 calls on one thread",
             "cpu": _cpu_model()}
 
 
@@ -214,6 +229,31 @@ def main():
         results[M] = dict(us=us, total_ms=total_ms, us_eager=us_eager, bytes=nb,
                           gbs=nb / (us * 1e-6) / 1e9, info=info)
 
+    # streaming-read ceiling over the M=1 call's byte count, same rotation and timing
+    nb1 = alg_bytes(N, K, bits, gs, 1)
+    SB = [torch.randint(0, 256, (nb1,), dtype=torch.uint8, device=dev) for _ in range(ncopies)]
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def launch_stream(i, M, stream, checksum=False):
+        st = q.stream_read_ptr(SB[i].data_ptr(), nb1, sink.data_ptr(), checksum, stream.cuda_stream)
+        if st != 0:
+            raise q.QmvError(st, "qmv_stream_read")
+
+    launch_stream(0, 1, torch.cuda.current_stream(), checksum=True)
+    torch.cuda.synchronize()
+    want = int(np.bitwise_xor.reduce(SB[0].cpu().numpy().view(np.uint32)))
+    assert (int(sink.item()) & 0xffffffff) == want, "stream-read checksum mismatch"
+    us_stream, _ = time_calls(launch_stream, ncopies, 1, args.steps, args.warmup, torch)
+    gbs_stream = nb1 / (us_stream * 1e-6) / 1e9
+    del SB
+
+    occupancy = {}
+    for M in (1, Mmax):
+        for R in (1, 2, 4):
+            inf = q.kernel_info(M, 17408, 5120, 4, 64, rows_per_wave=R)
+            occupancy[f"M{M}_R{R}"] = {k: inf[k] for k in ("vgprs", "lds_bytes", "waves_per_simd",
+                                                          "grid", "k_windows")}
+
     if args.calib_copy:
         a = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
         c = torch.empty_like(a)
@@ -253,6 +293,14 @@ def main():
             "traffic": traffic_for(1),
             "alg_bytes_per_launch": r1["bytes"],
         },
+        "stream_ceiling": {
+            "bytes": nb1,
+            "us_per_call": round(us_stream, 3),
+            "GB/s": round(gbs_stream, 1),
+            "frac_of_peak": round(gbs_stream / PEAK_GBS, 4),
+            "qmv_frac_of_ceiling": round(r1["gbs"] / gbs_stream, 4),
+        },
+        "occupancy_17408x5120": occupancy,
         "m13": {
             "M": Mmax,
             "us_per_call": round(r13["us"], 3),

@@ -4,7 +4,9 @@ The compute path is the HIP library ``lib/libqmv.so`` (C ABI in
 ``include/qmv.h``); ``qmv.py`` only marshals torch tensors into it.
 """
 from .qmv import (QmvError, affine, affine_ptr, kernel_info, status_string, library_path,
+                  stream_read_ptr,
                   DT_F32, DT_F16, DT_BF16, MAX_M)
 
 __all__ = ["QmvError", "affine", "affine_ptr", "kernel_info", "status_string", "library_path",
+           "stream_read_ptr",
            "DT_F32", "DT_F16", "DT_BF16", "MAX_M"]

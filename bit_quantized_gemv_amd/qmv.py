@@ -51,6 +51,8 @@ def lib():
         L.qmv_kernel_info.restype = I
         L.qmv_status_string.argtypes = [I]
         L.qmv_status_string.restype = ctypes.c_char_p
+        L.qmv_stream_read.argtypes = [P, ctypes.c_longlong, P, I, P]
+        L.qmv_stream_read.restype = I
         _lib = L
     return _lib
 
@@ -64,6 +66,13 @@ def affine_ptr(w, s, b, x, y, M, N, K, bits, group_size, x_dt=DT_BF16, sb_dt=DT_
     """Raw C-ABI call with integer device pointers; returns the status code."""
     return lib().qmv_affine_ex(w, s, b, x, y, M, N, K, bits, group_size, x_dt, sb_dt, y_dt,
                                rows_per_wave, stream)
+
+
+def stream_read_ptr(buf, nbytes, out, checksum=False, stream=0) -> int:
+    """Raw C-ABI call of the streaming-read ceiling kernel (a measurement aid):
+    reads the nbytes at device pointer buf; with checksum, XORs their XOR into
+    the uint32 at out."""
+    return lib().qmv_stream_read(buf, nbytes, out, 1 if checksum else 0, stream)
 
 
 def _dt_of(t, what):

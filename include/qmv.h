@@ -142,6 +142,19 @@ typedef struct {
 int qmv_kernel_info(int M, int N, int K, int bits, int group_size, qmv_dtype x_dt,
                     int rows_per_wave, qmv_kernel_info_t* out);
 
+/* Measurement aid, not part of the product: reads `bytes` bytes at `buf` (device
+ * memory, 16-byte aligned, bytes a positive multiple of 16) with the one-vector
+ * qmv's launch shape and 128-bit non-temporal loads.  Its time is the
+ * streaming-read ceiling a one-launch kernel of that shape reaches on that many
+ * bytes, against which the qmv's fraction of the HBM peak is read.  With
+ * `checksum` nonzero it also XORs the XOR of all 32-bit words of the buffer into
+ * *out (device memory, 4-byte aligned; clear it first), one atomic per
+ * wavefront on that one address -- slow, for checking; with `checksum` zero it
+ * only reads (it may store to *out).  Asynchronous on `stream`; one kernel
+ * launch, no other work.  Returns QMV_E_NULL, QMV_E_SHAPE, QMV_E_ALIGN or
+ * QMV_E_LAUNCH on bad arguments or a refused launch. */
+int qmv_stream_read(const void* buf, long long bytes, uint32_t* out, int checksum, void* stream);
+
 /* Static string naming a status code ("QMV_OK", "QMV_E_BITS", ...). */
 const char* qmv_status_string(int status);
 

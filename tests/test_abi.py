@@ -27,7 +27,7 @@ def L():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == ["qmv_affine", "qmv_affine_ex", "qmv_kernel_info",
-                                    "qmv_status_string"]
+                                    "qmv_status_string", "qmv_stream_read"]
 
 
 def test_exports_every_declared_symbol(L):
@@ -94,3 +94,15 @@ def test_binding_refuses_cpu_tensors():
     x = torch.zeros(1, 512, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         qmv.affine(w, s, s, x, bits=4, group_size=64)
+
+
+def test_stream_read_validates(L):
+    # argument errors return before any HIP call
+    P = ctypes.c_void_p
+    L.qmv_stream_read.argtypes = [P, ctypes.c_longlong, P, ctypes.c_int, P]
+    assert L.qmv_stream_read(None, 1024, 4096, 0, None) == 1          # QMV_E_NULL
+    assert L.qmv_stream_read(4096, 1024, None, 0, None) == 1
+    assert L.qmv_stream_read(4096, 1000, 8192, 0, None) == 4          # QMV_E_SHAPE: not whole 16-byte chunks
+    assert L.qmv_stream_read(4096, 0, 8192, 0, None) == 4
+    assert L.qmv_stream_read(4104, 1024, 8192, 0, None) == 6          # QMV_E_ALIGN
+    assert L.qmv_stream_read(4096, 1024, 8194, 0, None) == 6
