@@ -21,15 +21,17 @@
 //     compute of the unit PF places earlier, and a scheduling barrier keeps
 //     the compiler from sinking them below it.
 //   * A workgroup of W wavefronts stages the activations x[0..M)[K-window] in
-//     LDS, together with the group sums S[m][g], and walks row blocks of W*R
-//     rows (one per workgroup when the grid fits on the chip in one round).
+//     LDS, together with each chunk's dot-chain start and group sum, and walks
+//     row blocks of W*R rows (one per workgroup when the grid fits on the chip
+//     in one round).
 //     All activation loads are issued before the first weight load, and the
 //     weight prologue is in flight while the activations are converted.
-//   * Scales and biases are loaded on every lane (each lane reads the entry of
-//     its own group); lanes other than the group's owner zero them in
-//     registers.  Rows past N and chunks past a row's end read clamped,
-//     in-bounds addresses; the activations and group sums of chunks past the
-//     row's end are zero in LDS, so those lanes add nothing.
+//   * Each lane loads the scale and bias of its own group: of every row (and
+//     zeroes them in registers where it does not own the group), or, with
+//     paired rows (step 4 below), of the rows it owns.  Rows past N and chunks
+//     past a row's end read clamped, in-bounds addresses; the activations,
+//     chain starts and group sums of chunks past the row's end are zero in
+//     LDS, so those lanes add nothing.
 //   * The weight decode of a chunk happens once per step, outside the loop over
 //     the M vectors; every vector then reuses the decoded registers.
 //
@@ -43,7 +45,7 @@
 //      ends at the chunk's raw integer dot sum_k q_k x_k.  Pair j of a word
 //      holds fields (j, j + 32/(2 bits)); the matching activation pairs are
 //      laid out that way in LDS.
-//      fp32 activations: D'_c is the fma chain over the chunk's values in
+//      fp32 activations: D_c is the fma chain over the chunk's values in
 //      ascending k, from 0, with exact fp32 codes.
 //   2. The lpg = gs*bits/128 chunks of a group sit in adjacent lanes; their
 //      partials are combined by a DPP butterfly (xor 1, then xor 2).
@@ -283,8 +285,8 @@ __device__ __forceinline__ int after(int v, float dep)
 
 // ------------------------------------------------------ activation staging
 // Stages x[0..M)[window] into LDS (bf16 pairs in code-pair order, or fp32 in
-// natural order), writes S[m][group] for the window's groups, and zeroes the
-// activations and group sums of the window's chunks past the row's end.
+// natural order), writes each chunk's (dot-chain start, group sum) pair, and
+// zeroes the activations and pairs of the window's chunks past the row's end.
 // Work is cut into units of UV consecutive values of one vector; a round is
 // one unit per thread of one vector's window.  The loads of up to XB rounds
 // are issued together before any of them is consumed.
@@ -480,7 +482,7 @@ __device__ __forceinline__ float xor_lanes(float v)
 
 constexpr int pow2_at_least(int v) { return v <= 1 ? 1 : 2 * pow2_at_least((v + 1) / 2); }
 
-// Row totals of V = R*M per-lane partials, all at once.  Every value is summed
+// Row totals of V per-lane partials (rows x vectors), all at once.  Every value is summed
 // over the 64 lanes by the same tree -- pairs of lanes l, l ^ d combined for
 // d = 32, 16, 8, 4, 2, 1 in that order -- so a value's bits do not depend on
 // how many other values share the reduction.  While several values remain per
@@ -488,6 +490,9 @@ constexpr int pow2_at_least(int v) { return v <= 1 ? 1 : 2 * pow2_at_least((v + 
 // keeps a different value than lane l ^ d; once one value remains, the level
 // is a butterfly.  On return, v[0] of lane l holds the total of value
 // reduce_index<P>(l); lanes l with l % (64/P) == 0 hold distinct values.
+// PAIRS: lanes l and l ^ 1 hold partials of different rows (paired folds);
+// the levels d = 32 .. 2 run as above and the xor-1 level is the add of the
+// +0 that lane l ^ 1 would contribute to lane l's row.
 template <int P, bool PAIRS = false>
 __device__ __forceinline__ void lane_reduce(float (&v)[P], int lane)
 {
