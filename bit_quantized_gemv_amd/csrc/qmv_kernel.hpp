@@ -843,24 +843,24 @@ void qmv_affine_kernel(const Params p)
                                 }
                             }
                         } else {
-    #pragma unroll
+#pragma unroll
                             for (int r = 0; r < R; ++r) {
                                 const uint32_t wd[4] = {wcur[r].x, wcur[r].y, wcur[r].z, wcur[r].w};
                                 float d[M];
-    #pragma unroll
+#pragma unroll
                                 for (int m = 0; m < M; ++m) d[m] = c0[m];
-    #pragma unroll
+#pragma unroll
                                 for (int i = 0; i < 4; ++i) {
                                     uint32_t qw[PPW];
-    #pragma unroll
+#pragma unroll
                                     for (int j = 0; j < PPW; ++j) qw[j] = code_pair<BITS>(wd[i], j, magic);
-    #pragma unroll
+#pragma unroll
                                     for (int m = 0; m < M; ++m)
-    #pragma unroll
+#pragma unroll
                                         for (int j = 0; j < PPW; ++j) d[m] = dot2(qw[j], xp[m][i * PPW + j], d[m]);
                                     __builtin_amdgcn_sched_barrier(0);
                                 }
-    #pragma unroll
+#pragma unroll
                                 for (int m = 0; m < M; ++m) {
                                     const float dd = lane_group_sum<LPG>(d[m]);
                                     acc[r][m] = pinned(__builtin_fmaf(sv[r], dd, __builtin_fmaf(bv[r], S[m], acc[r][m])));
