@@ -44,6 +44,9 @@ if ROOT not in sys.path:
 METRIC = "achieved HBM GB/s (% of peak) and µs/call for 4-bit qmv at M=1 and M=13"
 WORKLOAD = "up_4b_15360x3840"
 PEAK_GBS = 8000.0           # MI355X HBM3E
+# Vector-ALU peak of the dot products: 256 CUs x 64 lanes x 2.4 GHz, one
+# v_dot2_f32_bf16 (2 multiply-adds = 4 flops) per lane per cycle.
+PEAK_DOT_TFLOPS = 256 * 64 * 2.4e9 * 4 / 1e12
 ROTATE_BYTES = 1 << 30      # >= 4x the 256 MB Infinity Cache
 KERNEL_SOURCES = ("bit_quantized_gemv_amd/csrc/qmv_kernel.hpp",)
 
@@ -315,6 +318,13 @@ def main():
             "alg_bytes_per_launch": r13["bytes"],
             "us_per_call_eager": round(r13["us_eager"], 3),
             "valu_TFLOPs_dot": round(flops13 / (r13["us"] * 1e-6) / 1e12, 2),
+            "roofline_alu": {
+                "bound": "alu",
+                "achieved": round(flops13 / (r13["us"] * 1e-6) / 1e12, 2),
+                "peak": round(PEAK_DOT_TFLOPS, 1),
+                "unit": "TFLOP/s",
+                "frac": round(flops13 / (r13["us"] * 1e-6) / 1e12 / PEAK_DOT_TFLOPS, 4),
+            },
             "traffic": traffic_for(Mmax),
             "kernel": r13["info"],
         },
