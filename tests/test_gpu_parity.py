@@ -29,6 +29,8 @@ SMALL = [  # N, K, bits, gs, sb, x, Ms
     (5, 64, 4, 64, "f16", "bf16", (1, 2)),             # one group per row
     (3, 128, 2, 128, "bf16", "f32", (1, 3)),
     (200, 8192, 2, 64, "bf16", "bf16", (6,)),          # 2 full wave steps at 2 bits
+    (8, 1 << 20, 4, 128, "bf16", "bf16", (1, 13)),      # the largest K: 512 wave steps, hundreds of K windows
+    (96, 131072, 2, 64, "f16", "bf16", (2, 13)),        # long K at 2 bits: many windows, restaged per window
 ]
 
 
