@@ -29,7 +29,7 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb)
     return a0 < b0 + nb && b0 < a0 + na;
 }
 
-int r_index(int R) { return R == 1 ? 0 : (R == 2 ? 1 : 2); }
+int r_index(int R) { return R - 1; }   // R in 1..4
 
 // Pure argument check (no HIP calls).
 int check_args(const uint32_t* w, const void* s, const void* b, const void* x, void* y, int M,
@@ -43,7 +43,7 @@ int check_args(const uint32_t* w, const void* s, const void* b, const void* x, v
     if (x_dt != QMV_DT_F32 && x_dt != QMV_DT_BF16) return QMV_E_DTYPE;
     if (sb_dt != QMV_DT_F16 && sb_dt != QMV_DT_BF16) return QMV_E_DTYPE;
     if (y_dt != QMV_DT_F32 && y_dt != QMV_DT_BF16) return QMV_E_DTYPE;
-    if (R != 0 && R != 1 && R != 2 && R != 4) return QMV_E_ROWS;
+    if (R < 0 || R > 4) return QMV_E_ROWS;
     const long long G = K / gs;
     if (!aligned(w, 16) || !aligned(s, 16) || !aligned(b, 16) || !aligned(x, 16)) return QMV_E_ALIGN;
     if (!aligned(y, (size_t)dtype_bytes(y_dt))) return QMV_E_ALIGN;
@@ -238,7 +238,7 @@ int choose_plan(int M, int N, int K, int bits, int gs, bool xf32, bool sbf, int 
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return QMV_E_LAUNCH;
     const int cus = cu_count(dev);
-    if (bits == 2 && R_req == 4) R_req = 2;
+    if (bits == 2 && R_req >= 3) R_req = 2;      // no three- or four-row 2-bit instances
     bool shape_ok = false;
     auto take = [&](int R, int W, int PF) -> int {
         if (R_req != 0 && R != R_req) return 0;
@@ -249,7 +249,7 @@ int choose_plan(int M, int N, int K, int bits, int gs, bool xf32, bool sbf, int 
         return 1;
     };
     if (M <= 2) {
-        const int Rs[3] = {2, 1, 4};
+        const int Rs[4] = {2, 1, 4, 3};
         for (int R : Rs)
             for (int W = qmv::kMaxWaves; W >= 1; --W) {
                 const int st = take(R, W, 1);
@@ -257,13 +257,13 @@ int choose_plan(int M, int N, int K, int bits, int gs, bool xf32, bool sbf, int 
                 if (st > 0) return QMV_OK;
             }
     } else {
-        const int Rs[3] = {4, 2, 1};
-        const double cost[3] = {1.0, 1.1, 2.5};
+        const int Rs[4] = {4, 3, 2, 1};
+        const double cost[4] = {1.0, 1.2, 1.1, 2.5};
         double best_score = 0.0;
         bool found = false;
-        for (int i = 0; i < 3; ++i) {
+        for (int i = 0; i < 4; ++i) {
             const int R = Rs[i];
-            if ((R_req != 0 && R != R_req) || (bits == 2 && R == 4)) continue;
+            if ((R_req != 0 && R != R_req) || (bits == 2 && R >= 3)) continue;
             for (int W = qmv::kMaxWaves; W >= 1; --W) {
                 Plan pl;
                 const int st = try_plan(M, N, K, bits, gs, xf32, sbf, R, W, 1, dev, cus, pl, shape_ok);

@@ -10,7 +10,7 @@
 namespace qmv {
 
 using KernelFn = void (*)(Params);
-constexpr int kNumR = 3;      // rows per wavefront 1, 2, 4
+constexpr int kNumR = 4;      // rows per wavefront 1, 2, 3, 4
 constexpr int kNumPF = 3;     // units in flight per wavefront 1, 2, 4
 constexpr int kMaxM = 13;
 constexpr int kNumSb = 2;     // scales/biases fp16, bf16

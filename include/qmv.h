@@ -73,7 +73,7 @@ enum {
                            is not aligned to its element size */
     QMV_E_DTYPE = 7,    /* unsupported dtype (x: f32/bf16; scales and biases:
                            f16/bf16; y: f32/bf16) */
-    QMV_E_ROWS = 8,     /* rows_per_wave is not 0, 1, 2 or 4 */
+    QMV_E_ROWS = 8,     /* rows_per_wave is not 0, 1, 2, 3 or 4 */
     QMV_E_ALIAS = 9,    /* y overlaps an input buffer */
     QMV_E_LAUNCH = 10   /* the HIP runtime refused the launch (e.g. no gfx950 device) */
 };
@@ -107,8 +107,8 @@ int qmv_affine(const uint32_t* w_packed, const void* scales, const void* biases,
  * Same operation and kernel family with explicit dtypes and row blocking.
  *   x_dt: QMV_DT_F32 or QMV_DT_BF16; sb_dt (scales and biases): QMV_DT_F16 or
  *   QMV_DT_BF16; y_dt: QMV_DT_F32 or QMV_DT_BF16.
- *   rows_per_wave: output rows owned by one wavefront (1, 2 or 4), or 0 for the
- *   library's choice.  It changes the launch shape only, never the result
+ *   rows_per_wave: output rows owned by one wavefront (1, 2, 3 or 4; 2-bit codes
+ *   use at most 2), or 0 for the library's choice.  It changes the launch shape only, never the result
  *   (mlxcel PR "block output rows per warp in qmv below Ampere", section "What
  *   lands": row blocking leaves the per-row arithmetic untouched).
  */

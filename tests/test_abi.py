@@ -71,7 +71,7 @@ def call(L, w=W, s=SC, b=BI, x=X, y=Y, **kw):
     (dict(w=W + 8), 6), (dict(s=SC + 4), 6), (dict(b=BI + 2), 6), (dict(x=X + 8), 6),
     (dict(y=Y + 1), 6), (dict(y=Y + 2, ydt=0), 6),
     (dict(xdt=1), 7), (dict(xdt=5), 7), (dict(sdt=0), 7), (dict(ydt=1), 7),
-    (dict(R=3), 8), (dict(R=8), 8), (dict(R=-1), 8),
+    (dict(R=5), 8), (dict(R=8), 8), (dict(R=-1), 8),
     (dict(y=X), 9), (dict(y=W + 64), 9), (dict(y=SC - 16), 9),
 ])
 def test_rejects_bad_arguments(L, kw, code):

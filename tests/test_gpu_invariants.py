@@ -39,9 +39,9 @@ def test_rows_per_wave_invariance(name):
     dev = U.to_dev(p)
     for M in (1, 5, 13):
         U.say(f"R-invariance {name} M={M}")
-        ys = [U.gpu(p, dev, M, torch.float32, R=R) for R in (1, 2, 4)]
-        assert torch.equal(_bits(ys[0]), _bits(ys[1]))
-        assert torch.equal(_bits(ys[0]), _bits(ys[2]))
+        ys = [U.gpu(p, dev, M, torch.float32, R=R) for R in (1, 2, 3, 4)]
+        for i in (1, 2, 3):
+            assert torch.equal(_bits(ys[0]), _bits(ys[i])), f"R index {i}"
 
 
 def test_run_to_run_determinism():
@@ -76,7 +76,7 @@ def test_error_status_on_gpu():
     with pytest.raises(q.QmvError):
         q.affine(w, s, b, x[:13], bits=3, group_size=64)
     with pytest.raises(q.QmvError):
-        q.affine(w, s, b, x[:5], bits=4, group_size=64, rows_per_wave=3)
+        q.affine(w, s, b, x[:5], bits=4, group_size=64, rows_per_wave=5)
 
 
 @pytest.mark.parametrize("name", ["tiny_4b_g64", "up_4b_15360x3840", "up_2b_15360x3840"])
