@@ -258,7 +258,7 @@ def main():
 
     occupancy = {}
     for M in (1, Mmax):
-        for R in (1, 2, 4):
+        for R in (1, 2, 3, 4):
             inf = q.kernel_info(M, 17408, 5120, 4, 64, rows_per_wave=R)
             occupancy[f"M{M}_R{R}"] = {k: inf[k] for k in ("vgprs", "lds_bytes", "waves_per_simd",
                                                           "grid", "k_windows")}
