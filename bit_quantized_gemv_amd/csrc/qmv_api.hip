@@ -220,10 +220,12 @@ int try_plan(int M, int N, int K, int bits, int gs, bool xf32, bool sbf, int R, 
 
 // Launch shape (measured on MI355X over the 12B- and 27B-class projection
 // shapes; an explicit rows-per-wavefront request is honoured in both cases):
-//   * M <= 2, bound by memory: two rows per wavefront, 8 wavefronts, one unit
-//     in flight (the best or within a few percent of the best launch on every
-//     measured shape); one row when two have no instance, fewer wavefronts
-//     when 8 do not fit.
+//   * M <= 2, bound by memory: 8 wavefronts, one unit in flight, and the rows
+//     per wavefront that put the fewest rows on the busiest compute unit
+//     (ties: 2, 3, 1, 4 rows; one row's many small workgroups measure slower
+//     than three rows at equal rows per CU).  Two rows on most shapes; three
+//     on 5120 rows (214 workgroups of 24 rows instead of 320 of 16, 16%
+//     faster); fewer wavefronts when 8 do not fit.
 //   * M >= 3, bound by the vector ALUs: 8 wavefronts, one unit in flight, and
 //     the R that minimises the rows the busiest compute unit processes,
 //     weighted by the per-row cost of fewer rows per wavefront (the
@@ -240,22 +242,29 @@ int choose_plan(int M, int N, int K, int bits, int gs, bool xf32, bool sbf, int 
     const int cus = cu_count(dev);
     if (bits == 2 && R_req >= 3) R_req = 2;      // no three- or four-row 2-bit instances
     bool shape_ok = false;
-    auto take = [&](int R, int W, int PF) -> int {
-        if (R_req != 0 && R != R_req) return 0;
-        Plan pl;
-        const int st = try_plan(M, N, K, bits, gs, xf32, sbf, R, W, PF, dev, cus, pl, shape_ok);
-        if (st <= 0) return st;
-        best = pl;
-        return 1;
-    };
     if (M <= 2) {
-        const int Rs[4] = {2, 1, 4, 3};
-        for (int R : Rs)
+        // bound by memory: rows are equally cheap at any R, so the R that puts
+        // the fewest rows on the busiest compute unit, ties in this order
+        const int Rs[4] = {2, 3, 1, 4};
+        int best_rows = 0;
+        bool found = false;
+        for (int R : Rs) {
+            if ((R_req != 0 && R != R_req) || (bits == 2 && R >= 3)) continue;
             for (int W = qmv::kMaxWaves; W >= 1; --W) {
-                const int st = take(R, W, 1);
+                Plan pl;
+                const int st = try_plan(M, N, K, bits, gs, xf32, sbf, R, W, 1, dev, cus, pl, shape_ok);
                 if (st < 0) return QMV_E_LAUNCH;
-                if (st > 0) return QMV_OK;
+                if (st == 0) continue;
+                const int rows_cu = ((pl.p.n_rb + cus - 1) / cus) * W * R;
+                if (!found || rows_cu < best_rows) {
+                    found = true;
+                    best_rows = rows_cu;
+                    best = pl;
+                }
+                break;
             }
+        }
+        if (found) return QMV_OK;
     } else {
         const int Rs[4] = {4, 3, 2, 1};
         const double cost[4] = {1.0, 1.2, 1.1, 2.5};
