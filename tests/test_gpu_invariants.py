@@ -113,3 +113,19 @@ def test_long_k_vectors_cut_into_whole_k_tiles():
     for m in (0, 6, 7, 12):
         one = U.gpu(p, dev, 1, torch.float32, x=dev[3][m:m + 1])
         assert torch.equal(_bits(y[m]), _bits(one[0])), f"vector {m}"
+
+
+@pytest.mark.parametrize("M,N,K,bits,gs,R,grid", [
+    (1, 15360, 3840, 4, 64, 2, 480),     # bench shape: two rows, two row blocks per workgroup
+    (13, 15360, 3840, 4, 64, 4, 240),    # bench shape at 13 vectors: four rows
+    (1, 5120, 17408, 4, 64, 3, 214),     # 5120 rows: three rows spread over 214 CUs
+    (13, 5120, 17408, 4, 64, 3, 214),
+    (1, 15360, 3840, 2, 128, 2, 480),    # 2 bits: two rows
+])
+def test_launch_shape_choices(M, N, K, bits, gs, R, grid):
+    # the planner's documented choices on an MI355X (256 CUs)
+    import torch as _t
+    if _t.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("launch-shape choices are documented for 256 compute units")
+    info = U.q.kernel_info(M, N, K, bits, gs)
+    assert (info["rows_per_wave"], info["grid"]) == (R, grid), info
