@@ -89,7 +89,6 @@ struct Plan {
 int make_plan(int M, int N, int K, int bits, int gs, bool xf32, bool sbf, int R, int W, int PF, Plan& pl)
 {
     const int G = K / gs;
-    const int lpg = gs * bits / 128;
     const int chunks = K * bits / 128;
     const int nsteps = (chunks + qmv::kWave - 1) / qmv::kWave;
     const int xcb = (128 / bits) * (xf32 ? 4 : 2);

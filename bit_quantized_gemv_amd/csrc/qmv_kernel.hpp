@@ -589,7 +589,6 @@ void qmv_affine_kernel(const Params p)
     constexpr int VPC = 128 / BITS;               // values per chunk
     constexpr int XCB = VPC * (XF32 ? 4 : 2);     // activation bytes per chunk in LDS
     constexpr int XSTEP = kWave * XCB + kWave * XCB / 16;  // padded LDS bytes per wave step
-    constexpr int OFFSET = 1 << BITS;             // code offset of the bf16 pairs
     constexpr int NS = PF + 1;                    // ring slots
     // Paired rows: with two lanes per group and an even number of rows, lane
     // parity selects the row a lane folds -- even lanes own the groups of rows
@@ -705,7 +704,6 @@ void qmv_affine_kernel(const Params p)
         for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
     int c_rb = 0, c_t = 0, c_tw = 0, c_win = 0;   // unit consumed next; its step within the window
     const int xl = lds_phys(lane * XCB);          // LDS offset of the lane's chunk in a window's first step
-    const int gl0 = lane / LPG;                   // group of the lane's chunk in a window's first step
     for (int ub = 0; ub < n_units; ub += NS) {
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
@@ -748,7 +746,6 @@ void qmv_affine_kernel(const Params p)
                         bv[k] = own ? fb : 0.0f;
                     }
                 }
-                const int gl = c_tw * (kWave / LPG) + gl0;    // group within the window
                 const int xo0 = xl + c_tw * XSTEP;            // chunk's LDS offset (never straddles padding)
                 const int cl = c_tw * kWave + lane;           // chunk within the window
 
