@@ -84,9 +84,10 @@ def traffic_for(M: int):
     return None if e is None else e.get("hbm_bytes")
 
 
-def time_calls(launch, ncopies, M, steps, warmup, torch):
+def time_calls(launch, ncopies, M, steps, warmup, torch, replays=1):
     """Per-call microseconds: K calls captured in one HIP graph, replayed
-    between HIP events on the capture/launch stream."""
+    between HIP events on the capture/launch stream (the median of `replays`
+    timed replays; one for the bench line, which times exactly K calls)."""
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
         for i in range(warmup):
@@ -99,16 +100,19 @@ def time_calls(launch, ncopies, M, steps, warmup, torch):
     stream.synchronize()
     g.replay()                       # first replay uploads the graph
     stream.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    with torch.cuda.stream(stream):
-        start.record(stream)
-        g.replay()
-        end.record(stream)
-    end.synchronize()
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end)
+    times = []
+    for _ in range(replays):
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            start.record(stream)
+            g.replay()
+            end.record(stream)
+        end.synchronize()
+        torch.cuda.synchronize()
+        times.append(start.elapsed_time(end))
+    ms = sorted(times)[len(times) // 2]
     return ms * 1000.0 / steps, ms
 
 
@@ -172,6 +176,42 @@ def _cpu_model():
     return None
 
 
+def workload_table(args, q, gen, torch, np, dev):
+    """Every 12B/27B-class workload at M = 1, 2, 4, 8, 13: us per call (graph
+    replay over rotating copies as in the bench line, median of three replays)
+    and the default launch."""
+    for name in ("up_4b_15360x3840", "down_4b_3840x15360", "up_2b_15360x3840",
+                 "up_4b_17408x5120", "down_4b_5120x17408"):
+        p = gen.make_problem(name)
+        N, K, bits, gs = p.N, p.K, p.bits, p.gs
+        per_copy = alg_bytes(N, K, bits, gs, 13)
+        nc = max(2, -(-ROTATE_BYTES // per_copy))
+        base = [torch.from_numpy(p.w_packed.view(np.int32)).to(dev),
+                torch.from_numpy(p.scales.view(np.int16)).view(torch.bfloat16).to(dev),
+                torch.from_numpy(p.biases.view(np.int16)).view(torch.bfloat16).to(dev),
+                torch.from_numpy(p.x.view(np.int16)).view(torch.bfloat16).to(dev)]
+        copies = [[t.clone() for t in base] + [torch.empty(13, N, dtype=torch.bfloat16, device=dev)]
+                  for _ in range(nc)]
+
+        def launch(i, M, stream):
+            w, s, b, x, y = (t.data_ptr() for t in copies[i])
+            st = q.affine_ptr(w, s, b, x, y, M, N, K, bits, gs, q.DT_BF16, q.DT_BF16, q.DT_BF16, 0,
+                              stream.cuda_stream)
+            if st != 0:
+                raise q.QmvError(st, "qmv_affine_ex")
+
+        for M in (1, 2, 4, 8, 13):
+            us, _ = time_calls(launch, nc, M, args.steps, args.warmup, torch, replays=3)
+            nb = alg_bytes(N, K, bits, gs, M)
+            inf = q.kernel_info(M, N, K, bits, gs)
+            print(json.dumps({"workload": name, "M": M, "us_per_call": round(us, 3),
+                              "GB/s": round(nb / (us * 1e-6) / 1e9, 1),
+                              "rows_per_wave": inf["rows_per_wave"], "wg_size": inf["wg_size"],
+                              "grid": inf["grid"], "k_windows": inf["k_windows"]}), flush=True)
+        del copies, base
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -181,6 +221,9 @@ def main():
                     help="time budget of the CPU-oracle baseline (0 = skip)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one plain 256 MiB device copy (HBM counter calibration)")
+    ap.add_argument("--table", action="store_true",
+                    help="instead of the bench line, time every workload at M = 1, 2, 4, 8, 13 with "
+                         "the library's default launch (one JSON line per case)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -195,6 +238,9 @@ def main():
 
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
+    if args.table:
+        workload_table(args, q, gen, torch, np, dev)
+        return
     wl = gen.WORKLOADS[WORKLOAD]
     p = gen.make_problem(WORKLOAD)
     N, K, bits, gs = p.N, p.K, p.bits, p.gs
