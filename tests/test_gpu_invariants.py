@@ -129,3 +129,32 @@ def test_launch_shape_choices(M, N, K, bits, gs, R, grid):
         pytest.skip("launch-shape choices are documented for 256 compute units")
     info = U.q.kernel_info(M, N, K, bits, gs)
     assert (info["rows_per_wave"], info["grid"]) == (R, grid), info
+
+
+def test_graph_capture_replays_match_eager():
+    # The calls can be captured in a HIP graph (one kernel launch per tile, no
+    # allocation, no memset): every replay, with eager work and new inputs in
+    # between, equals the eager call on the same inputs.
+    p = gen.make_problem("up_4b_15360x3840")
+    w, s, b, x = U.to_dev(p)
+    xs = gen.make_x(p.K, p.x_dtype, 77, rows=3 * 13)
+    xall = U.x_to_dev(xs, p.x_dtype)
+    xin = x[:13].clone()
+    y_graph = torch.empty(13, p.N, dtype=torch.float32, device=x.device)
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        U.q.affine(w, s, b, xin, bits=p.bits, group_size=p.gs, out=y_graph)      # warm-up
+    stream.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        U.q.affine(w, s, b, xin, bits=p.bits, group_size=p.gs, out=y_graph,
+                   stream=torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    for i in range(3):
+        U.say(f"graph replay {i}")
+        xin.copy_(xall[13 * i:13 * (i + 1)])
+        eager = U.gpu(p, (w, s, b, xall[13 * i:13 * (i + 1)]), 13, torch.float32)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(y_graph), _bits(eager)), f"replay {i}"
