@@ -59,11 +59,12 @@
 //      of the group with l % lpg == n % lpg -- as
 //      acc = fma(scale, D, fma(bias, S, acc)), over its groups in ascending
 //      step: the scale multiplies the group's raw integer dot D, the bias its
-//      activation sum S.  With lpg = 2 and an even number of rows per
-//      wavefront (and more than one vector), the two lanes of a group run the
-//      chains of both rows of a pair with the rows swapped on the odd lane, so
-//      one DPP add leaves each lane the group dot of its own row (the same two
-//      addends as step 2) and each lane folds only its own rows.  Otherwise
+//      activation sum S.  With lpg = 2 or 4, a multiple of lpg rows per
+//      wavefront and more than one vector, the lpg lanes of a group run the
+//      chains of all rows of a row group, in an order rotated by the lane's
+//      place in the group, so the DPP adds of step 2 (same addends, same
+//      grouping) leave each lane the group dot of its own row and each lane
+//      folds only its own rows.  Otherwise
 //      every lane executes the fold of every row, with scale and bias zeroed
 //      on lanes that do not own the group, which leaves their accumulators at
 //      +0.
@@ -490,14 +491,15 @@ constexpr int pow2_at_least(int v) { return v <= 1 ? 1 : 2 * pow2_at_least((v + 
 // keeps a different value than lane l ^ d; once one value remains, the level
 // is a butterfly.  On return, v[0] of lane l holds the total of value
 // reduce_index<P>(l); lanes l with l % (64/P) == 0 hold distinct values.
-// PAIRS: lanes l and l ^ 1 hold partials of different rows (paired folds);
-// the levels d = 32 .. 2 run as above and the xor-1 level is the add of the
-// +0 that lane l ^ 1 would contribute to lane l's row.
-template <int P, bool PAIRS = false>
+// SKIP > 0 (row-grouped folds): the lanes of each aligned group of 2^SKIP
+// lanes hold partials of different rows; the levels d = 32 .. 2^SKIP run as
+// above, and the levels below are the adds of the +0 that lanes owning none
+// of a row's groups contribute to it (one add of +0 gives the same bits).
+template <int P, int SKIP = 0>
 __device__ __forceinline__ void lane_reduce(float (&v)[P], int lane)
 {
     static_assert(P >= 1 && P <= 64 && (P & (P - 1)) == 0, "P must be a power of two <= 64");
-    static_assert(!PAIRS || P <= 32, "paired reductions hold at most 32 values");
+    static_assert(P <= (64 >> SKIP), "too many values for the lanes left");
     // d = 32
     if constexpr (P >= 2) {
 #pragma unroll
@@ -538,25 +540,21 @@ __device__ __forceinline__ void lane_reduce(float (&v)[P], int lane)
     };
     level(std::integral_constant<int, 8>{}, std::integral_constant<int, (P >= 8 ? P / 4 : 1)>{});
     level(std::integral_constant<int, 4>{}, std::integral_constant<int, (P >= 16 ? P / 8 : 1)>{});
-    level(std::integral_constant<int, 2>{}, std::integral_constant<int, (P >= 32 ? P / 16 : 1)>{});
-    if constexpr (!PAIRS) {
+    if constexpr (SKIP < 2)
+        level(std::integral_constant<int, 2>{}, std::integral_constant<int, (P >= 32 ? P / 16 : 1)>{});
+    if constexpr (SKIP < 1)
         level(std::integral_constant<int, 1>{}, std::integral_constant<int, (P >= 64 ? P / 32 : 1)>{});
-    } else {
-        // Lanes l and l ^ 1 hold different rows: the xor-1 level of a row's tree
-        // pairs each owner lane with a lane whose partial for that row is +0
-        // (it owns none of the row's groups), which leaves the value unchanged
-        // except that -0 becomes +0.
-        v[0] = v[0] + 0.0f;
-    }
+    // skipped levels: the value plus +0, i.e. unchanged except that -0 becomes +0
+    if constexpr (SKIP > 0) v[0] = v[0] + 0.0f;
 }
 
-// Which value lane l holds after lane_reduce<P, PAIRS>.
-template <int P, bool PAIRS = false>
+// Which value lane l holds after lane_reduce<P, SKIP>.
+template <int P, int SKIP = 0>
 __device__ __forceinline__ int reduce_index(int lane)
 {
     int idx = 0, n = P;
 #pragma unroll
-    for (int d = 32; d >= (PAIRS ? 2 : 1); d >>= 1) {
+    for (int d = 32; d >= (1 << SKIP); d >>= 1) {
         if (n >= 2) {
             if (lane & d) idx += n / 2;
             n /= 2;
@@ -590,19 +588,20 @@ void qmv_affine_kernel(const Params p)
     constexpr int XCB = VPC * (XF32 ? 4 : 2);     // activation bytes per chunk in LDS
     constexpr int XSTEP = kWave * XCB + kWave * XCB / 16;  // padded LDS bytes per wave step
     constexpr int NS = PF + 1;                    // ring slots
-    // Paired rows: with two lanes per group and an even number of rows, lane
-    // parity selects the row a lane folds -- even lanes own the groups of rows
-    // 2k, odd lanes those of rows 2k + 1 -- so each lane loads the metadata of
-    // R/2 rows, and one combine and one fold serve two rows.  (Every instance
-    // uses this ownership; unpaired ones zero the scale and bias of the rows a
-    // lane does not own, which gives the same bits.  One vector keeps the
-    // unpaired form: its short compute after the last load is latency-bound,
-    // and pairing adds the per-word lane selects to it.)
-    constexpr bool PAIRED = !XF32 && LPG == 2 && (R % 2 == 0) && M >= 2;
-    constexpr int RS = PAIRED ? R / 2 : R;        // rows each lane folds (accumulator sets)
+    // Row-grouped ("paired") folds: with lpg = 2 or 4 lanes per group and a
+    // multiple of lpg rows per wavefront, lane l of a group folds the rows
+    // lpg*k + l % lpg -- so each lane loads the metadata of R/lpg rows, and
+    // one combine and one fold serve lpg rows.  (Every instance uses this
+    // ownership; other instances zero the scale and bias of the rows a lane
+    // does not own, which gives the same bits.  One vector keeps that form:
+    // its short compute after the last load is latency-bound, and grouping
+    // adds the per-word lane selects to it.)
+    constexpr bool PAIRED = !XF32 && (R % LPG == 0) && ((LPG == 2 && M >= 2) || (LPG == 4 && M >= 9));
+    constexpr int RS = PAIRED ? R / LPG : R;      // rows each lane folds (accumulator sets)
+    constexpr int SKIP = PAIRED ? (LPG == 4 ? 2 : 1) : 0;   // reduction levels inside a group
     constexpr int V = RS * M;
     constexpr int P = pow2_at_least(V);
-    static_assert(P <= (PAIRED ? 32 : 64), "too many row totals per lane");
+    static_assert(P <= (64 >> SKIP), "too many row totals per lane");
 
     extern __shared__ __align__(16) uint8_t lds[];
     const int lane = threadIdx.x & (kWave - 1);
@@ -631,7 +630,7 @@ void qmv_affine_kernel(const Params p)
     const int row_step = grid * W * R;
     __amdgpu_buffer_rsrc_t i_wr, i_sr, i_br;
     int i_sw[R], i_ss[R];                            // per-row scalar offsets (weights, scales/biases)
-    int i_ps[RS];                                    // paired: offset of the lane's own row of each pair
+    int i_ps[RS];                                    // grouped: offset of the lane's own row of each row group
     auto set_block = [&]() {
         // every input of the resources is wave-uniform; readfirstlane makes that
         // explicit (a resource the compiler cannot prove uniform costs a
@@ -649,7 +648,7 @@ void qmv_affine_kernel(const Params p)
         }
         if constexpr (PAIRED) {
 #pragma unroll
-            for (int k = 0; k < RS; ++k) i_ps[k] = i_ss[2 * k] + (lane & 1) * (i_ss[2 * k + 1] - i_ss[2 * k]);
+            for (int k = 0; k < RS; ++k) i_ps[k] = min(k * LPG + lane % LPG, p.N - 1 - rbase) * p.G * 2;
         }
     };
     set_block();
@@ -788,6 +787,39 @@ void qmv_affine_kernel(const Params p)
                         d = lane_group_sum<LPG>(d);
                         a = pinned(__builtin_fmaf(sv[r], d, __builtin_fmaf(bv[r], S, a)));
                     };
+                    // Row groups (grouped folds): register j of group k holds row
+                    // LPG*k + (j ^ lane % LPG), so the lanes of a weight group run the
+                    // group's rows in rotated order.  `combine` adds, for the lane's own
+                    // row, its chain and its partners' -- xor 1 first, then xor 2 --
+                    // which are the addends and grouping of the plain butterfly.
+                    auto swap_words = [&](int k, int i, uint32_t (&out)[LPG]) {
+                        uint32_t w[LPG];
+#pragma unroll
+                        for (int t = 0; t < LPG; ++t) {
+                            const uint4& wr = wcur[PAIRED ? LPG * k + t : 0];
+                            w[t] = (i == 0) ? wr.x : (i == 1) ? wr.y : (i == 2) ? wr.z : wr.w;
+                        }
+                        const bool b0 = (lane & 1) != 0;
+#pragma unroll
+                        for (int t = 0; t < LPG; ++t) out[t] = b0 ? w[(t ^ 1) % LPG] : w[t];
+                        if constexpr (LPG == 4) {
+                            const bool b1 = (lane & 2) != 0;
+                            uint32_t a[LPG];
+#pragma unroll
+                            for (int t = 0; t < LPG; ++t) a[t] = out[t];
+#pragma unroll
+                            for (int t = 0; t < LPG; ++t) out[t] = b1 ? a[t ^ 2] : a[t];
+                        }
+                    };
+                    auto combine = [&](const float (&d)[LPG]) -> float {
+                        if constexpr (LPG <= 2) {
+                            return d[0] + dpp<kQuadXor1>(d[1 % LPG]);
+                        } else {
+                            const float w0 = d[0] + dpp<kQuadXor1>(d[1]);
+                            const float w1 = d[2 % LPG] + dpp<kQuadXor1>(d[3 % LPG]);
+                            return w0 + dpp<kQuadXor2>(w1);
+                        }
+                    };
                     if constexpr (M <= R) {
                         // few vectors: activation pairs of all M vectors first, then one
                         // row at a time, one weight word at a time: decode the word's
@@ -799,43 +831,37 @@ void qmv_affine_kernel(const Params p)
 #pragma unroll
                         for (int m = 0; m < M; ++m) read_x(m, xo0, xp[m], S[m], c0[m]);
                         if constexpr (PAIRED) {
-                            // rows 2k and 2k+1: an even lane runs chain X over row 2k's
-                            // chunk and chain Y over row 2k+1's, an odd lane the other way
-                            // round; X plus the partner lane's Y is then the group's dot of
-                            // the lane's own row
-                            const bool odd = (lane & 1) != 0;
 #pragma unroll
                             for (int k = 0; k < RS; ++k) {
-                                const uint32_t w0[4] = {wcur[2 * k].x, wcur[2 * k].y, wcur[2 * k].z, wcur[2 * k].w};
-                                const uint32_t w1[4] = {wcur[2 * k + 1].x, wcur[2 * k + 1].y, wcur[2 * k + 1].z, wcur[2 * k + 1].w};
-                                float dx[M], dy[M];
+                                float d[LPG][M];
 #pragma unroll
-                                for (int m = 0; m < M; ++m) {
-                                    dx[m] = c0[m];
-                                    dy[m] = c0[m];
-                                }
+                                for (int j = 0; j < LPG; ++j)
+#pragma unroll
+                                    for (int m = 0; m < M; ++m) d[j][m] = c0[m];
 #pragma unroll
                                 for (int i = 0; i < 4; ++i) {
-                                    const uint32_t wa = odd ? w1[i] : w0[i];
-                                    const uint32_t wb2 = odd ? w0[i] : w1[i];
-                                    uint32_t qa[PPW], qb[PPW];
+                                    uint32_t ws[LPG];
+                                    swap_words(k, i, ws);
+                                    uint32_t q[LPG][PPW];
 #pragma unroll
-                                    for (int j = 0; j < PPW; ++j) {
-                                        qa[j] = code_pair<BITS>(wa, j, magic);
-                                        qb[j] = code_pair<BITS>(wb2, j, magic);
-                                    }
+                                    for (int j = 0; j < LPG; ++j)
+#pragma unroll
+                                        for (int jj = 0; jj < PPW; ++jj) q[j][jj] = code_pair<BITS>(ws[j], jj, magic);
 #pragma unroll
                                     for (int m = 0; m < M; ++m)
 #pragma unroll
-                                        for (int j = 0; j < PPW; ++j) {
-                                            dx[m] = dot2(qa[j], xp[m][i * PPW + j], dx[m]);
-                                            dy[m] = dot2(qb[j], xp[m][i * PPW + j], dy[m]);
-                                        }
+                                        for (int jj = 0; jj < PPW; ++jj)
+#pragma unroll
+                                            for (int j = 0; j < LPG; ++j)
+                                                d[j][m] = dot2(q[j][jj], xp[m][i * PPW + jj], d[j][m]);
                                     __builtin_amdgcn_sched_barrier(0);
                                 }
 #pragma unroll
                                 for (int m = 0; m < M; ++m) {
-                                    const float dd = dx[m] + dpp<kQuadXor1>(dy[m]);
+                                    float dv[LPG];
+#pragma unroll
+                                    for (int j = 0; j < LPG; ++j) dv[j] = d[j][m];
+                                    const float dd = combine(dv);
                                     acc[k][m] = pinned(__builtin_fmaf(sv[k], dd, __builtin_fmaf(bv[k], S[m], acc[k][m])));
                                 }
                             }
@@ -885,18 +911,14 @@ void qmv_affine_kernel(const Params p)
                         read_xr(0, xo0, xq[0], Sq[0], cq[0]);
                         uint32_t qp[R][NP];
                         if constexpr (PAIRED) {
-                            // chain registers 2k / 2k+1 hold rows 2k / 2k+1 on even lanes
-                            // and rows 2k+1 / 2k on odd lanes (see the few-vector path)
-                            const bool odd = (lane & 1) != 0;
 #pragma unroll
                             for (int k = 0; k < RS; ++k) {
-                                const uint4 w0 = wcur[2 * k], w1 = wcur[2 * k + 1];
-                                const uint4 wa = make_uint4(odd ? w1.x : w0.x, odd ? w1.y : w0.y,
-                                                            odd ? w1.z : w0.z, odd ? w1.w : w0.w);
-                                const uint4 wb2 = make_uint4(odd ? w0.x : w1.x, odd ? w0.y : w1.y,
-                                                             odd ? w0.z : w1.z, odd ? w0.w : w1.w);
-                                decode(wa, qp[2 * k]);
-                                decode(wb2, qp[2 * k + 1]);
+                                uint32_t ws[4][LPG];
+#pragma unroll
+                                for (int i = 0; i < 4; ++i) swap_words(k, i, ws[i]);
+#pragma unroll
+                                for (int j = 0; j < LPG; ++j)
+                                    decode(make_uint4(ws[0][j], ws[1][j], ws[2][j], ws[3][j]), qp[LPG * k + j]);
                             }
                         } else {
 #pragma unroll
@@ -918,7 +940,10 @@ void qmv_affine_kernel(const Params p)
                                 }
 #pragma unroll
                                 for (int k = 0; k < RS; ++k) {
-                                    const float dd = d[2 * k] + dpp<kQuadXor1>(d[2 * k + 1]);
+                                    float dv[LPG];
+#pragma unroll
+                                    for (int j = 0; j < LPG; ++j) dv[j] = d[PAIRED ? LPG * k + j : 0];
+                                    const float dd = combine(dv);
                                     acc[k][m] = pinned(__builtin_fmaf(sv[k], dd, __builtin_fmaf(bv[k], Sq[m & 1], acc[k][m])));
                                 }
                             } else {
@@ -993,11 +1018,11 @@ void qmv_affine_kernel(const Params p)
                     float v[P];
 #pragma unroll
                     for (int i = 0; i < P; ++i) v[i] = (i < V) ? acc[i / M][i % M] : 0.0f;
-                    lane_reduce<P, PAIRED>(v, lane);
-                    const int idx = reduce_index<P, PAIRED>(lane);
+                    lane_reduce<P, SKIP>(v, lane);
+                    const int idx = reduce_index<P, SKIP>(lane);
                     const int k = idx / M, m = idx - (idx / M) * M;
-                    const int r = PAIRED ? 2 * k + (lane & 1) : k;
-                    const bool holder = PAIRED ? ((lane >> 1) % (32 / P)) == 0 : (lane % (64 / P)) == 0;
+                    const int r = PAIRED ? LPG * k + lane % LPG : k;
+                    const bool holder = ((lane >> SKIP) % ((64 >> SKIP) / P)) == 0;
                     if (holder && idx < V && rb0 + r < p.N) {
                         const size_t o = (size_t)m * p.N + rb0 + r;
                         if (p.y_bf16)

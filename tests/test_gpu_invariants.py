@@ -32,13 +32,17 @@ def test_m_invariance(name):
             assert torch.equal(_bits(y16[m]), _bits(U.rne_bf16(ones[m][0])))
 
 
-@pytest.mark.parametrize("name", ["up_4b_15360x3840", "down_4b_3840x15360", "up_2b_15360x3840",
-                                  "up_4b_17408x5120", "down_4b_5120x17408"])
-def test_rows_per_wave_invariance(name):
-    p = gen.make_problem(name)
+@pytest.mark.parametrize("name,gs", [
+    ("up_4b_15360x3840", None), ("down_4b_3840x15360", None), ("up_2b_15360x3840", None),
+    ("up_4b_17408x5120", None), ("down_4b_5120x17408", None),
+    # 4-bit codes in groups of 128: four lanes per group (row groups of four at R = 4)
+    ("up_4b_15360x3840", 128), ("down_4b_5120x17408", 128),
+])
+def test_rows_per_wave_invariance(name, gs):
+    p = gen.make_problem(name, gs=gs)
     dev = U.to_dev(p)
-    for M in (1, 5, 13):
-        U.say(f"R-invariance {name} M={M}")
+    for M in (1, 2, 5, 13):
+        U.say(f"R-invariance {name} gs={p.gs} M={M}")
         ys = [U.gpu(p, dev, M, torch.float32, R=R) for R in (1, 2, 3, 4)]
         for i in (1, 2, 3):
             assert torch.equal(_bits(ys[0]), _bits(ys[i])), f"R index {i}"

@@ -48,6 +48,29 @@ def test_small_vs_oracle(case):
         assert torch.equal(y16.view(torch.int16), U.rne_bf16(y32).view(torch.int16))
 
 
+@pytest.mark.parametrize("N,K,bits,gs,sb", [
+    (67, 2560, 4, 128, "bf16"),     # four lanes per group; 67 rows: a ragged row group
+    (130, 1536, 4, 128, "f16"),
+    (61, 2560, 4, 64, "bf16"),      # two lanes per group
+    (45, 4608, 2, 128, "bf16"),
+])
+def test_every_rows_per_wave_vs_oracle(N, K, bits, gs, sb):
+    # every row blocking (1-4 rows per wavefront; 2-bit codes up to 2) against the
+    # oracle, and bit-identical to each other, at M = 1 .. 13 with bf16 activations
+    p = gen.make_problem(N=N, K=K, bits=bits, gs=gs, sb=sb, x_dtype="bf16", seed=N * 5 + K)
+    dev = U.to_dev(p)
+    Rs = (1, 2, 3, 4) if bits == 4 else (1, 2)
+    for M in (1, 2, 3, 4, 8, 13):
+        want = U.ref(p, M)
+        ys = []
+        for R in Rs:
+            U.say(f"rows per wave N={N} K={K} bits={bits} gs={gs} M={M} R={R}")
+            ys.append(U.gpu(p, dev, M, torch.float32, R=R))
+        U.check_parity(ys[0], want, f"M={M}")
+        for R, y in zip(Rs[1:], ys[1:]):
+            assert torch.equal(y.view(torch.int32), ys[0].view(torch.int32)), f"M={M} R={R}"
+
+
 WORKLOADS = [n for n in gen.WORKLOADS if n != "tiny_4b_g64"]
 
 
