@@ -217,6 +217,15 @@ int try_plan(int M, int N, int K, int bits, int gs, bool xf32, bool sbf, int R, 
     return 1;
 }
 
+// Rows the busiest compute unit processes: workgroups are dealt out whole, so
+// a compute unit holds up to ceil(grid / CUs) of them, each covering `per` row
+// blocks of W*R rows.
+int busiest_cu_rows(const Plan& pl, int cus)
+{
+    const int per = (pl.p.n_rb + pl.grid - 1) / pl.grid;
+    return ((pl.grid + cus - 1) / cus) * per * pl.W * pl.R;
+}
+
 // Launch shape (measured on MI355X over the 12B- and 27B-class projection
 // shapes; an explicit rows-per-wavefront request is honoured in both cases):
 //   * M <= 2, bound by memory: 8 wavefronts, one unit in flight, and the rows
@@ -224,14 +233,17 @@ int try_plan(int M, int N, int K, int bits, int gs, bool xf32, bool sbf, int R, 
 //     (ties: 2, 3, 1, 4 rows; one row's many small workgroups measure slower
 //     than three rows at equal rows per CU).  Two rows on most shapes; three
 //     on 5120 rows (214 workgroups of 24 rows instead of 320 of 16, 16%
-//     faster); fewer wavefronts when 8 do not fit.
+//     faster); one on 17408 rows (726 workgroups of three 8-row blocks, at
+//     most 72 rows per CU, instead of 363 workgroups of two 24-row blocks,
+//     which leave 107 CUs with two workgroups and 96 rows: 14% faster at one
+//     vector); fewer wavefronts when 8 do not fit.
 //   * M >= 3, bound by the vector ALUs: 8 wavefronts, one unit in flight, and
 //     the R that minimises the rows the busiest compute unit processes,
 //     weighted by the per-row cost of fewer rows per wavefront (the
-//     activations read from LDS and the decode are shared by fewer rows): 1.1x
-//     for two rows and 2.5x for one row, relative to four (one row per
-//     wavefront reads the activations from LDS once per row, which makes it
-//     LDS-bound where the vector ALUs are busy).
+//     activations read from LDS and the decode are shared by fewer rows): 1.2x
+//     for three rows (ungrouped folds), 1.1x for two and 2.5x for one,
+//     relative to four (one row per wavefront reads the activations from LDS
+//     once per row, which makes it LDS-bound where the vector ALUs are busy).
 //   * 2-bit codes have no four-row instances; K-windowed calls have one unit
 //     in flight.
 int choose_plan(int M, int N, int K, int bits, int gs, bool xf32, bool sbf, int R_req, Plan& best)
@@ -254,7 +266,7 @@ int choose_plan(int M, int N, int K, int bits, int gs, bool xf32, bool sbf, int 
                 const int st = try_plan(M, N, K, bits, gs, xf32, sbf, R, W, 1, dev, cus, pl, shape_ok);
                 if (st < 0) return QMV_E_LAUNCH;
                 if (st == 0) continue;
-                const int rows_cu = ((pl.p.n_rb + cus - 1) / cus) * W * R;
+                const int rows_cu = busiest_cu_rows(pl, cus);
                 if (!found || rows_cu < best_rows) {
                     found = true;
                     best_rows = rows_cu;
@@ -277,9 +289,7 @@ int choose_plan(int M, int N, int K, int bits, int gs, bool xf32, bool sbf, int 
                 const int st = try_plan(M, N, K, bits, gs, xf32, sbf, R, W, 1, dev, cus, pl, shape_ok);
                 if (st < 0) return QMV_E_LAUNCH;
                 if (st == 0) continue;
-                const int n_rb = pl.p.n_rb;
-                const double rows_cu = (double)((n_rb + cus - 1) / cus) * W * R;
-                const double score = rows_cu * cost[i];
+                const double score = busiest_cu_rows(pl, cus) * cost[i];
                 if (!found || score < best_score - 1e-9) {
                     found = true;
                     best_score = score;

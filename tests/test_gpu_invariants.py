@@ -124,6 +124,7 @@ def test_long_k_vectors_cut_into_whole_k_tiles():
     (13, 15360, 3840, 4, 64, 4, 240),    # bench shape at 13 vectors: four rows
     (1, 5120, 17408, 4, 64, 3, 214),     # 5120 rows: three rows spread over 214 CUs
     (13, 5120, 17408, 4, 64, 3, 214),
+    (1, 17408, 5120, 4, 64, 1, 726),     # 17408 rows: one row, three 8-row blocks per workgroup
     (1, 15360, 3840, 2, 128, 2, 480),    # 2 bits: two rows
 ])
 def test_launch_shape_choices(M, N, K, bits, gs, R, grid):
