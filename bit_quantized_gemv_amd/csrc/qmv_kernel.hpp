@@ -28,7 +28,7 @@
 //     weight prologue is in flight while the activations are converted.
 //   * Each lane loads the scale and bias of its own group: of every row (and
 //     zeroes them in registers where it does not own the group), or, with
-//     paired rows (step 4 below), of the rows it owns.  Rows past N and chunks
+//     grouped rows (step 4 below), of the rows it owns.  Rows past N and chunks
 //     past a row's end read clamped, in-bounds addresses; the activations,
 //     chain starts and group sums of chunks past the row's end are zero in
 //     LDS, so those lanes add nothing.
@@ -588,7 +588,7 @@ void qmv_affine_kernel(const Params p)
     constexpr int XCB = VPC * (XF32 ? 4 : 2);     // activation bytes per chunk in LDS
     constexpr int XSTEP = kWave * XCB + kWave * XCB / 16;  // padded LDS bytes per wave step
     constexpr int NS = PF + 1;                    // ring slots
-    // Row-grouped ("paired") folds: with lpg = 2 or 4 lanes per group and a
+    // Grouped folds: with lpg = 2 or 4 lanes per group and a
     // multiple of lpg rows per wavefront, lane l of a group folds the rows
     // lpg*k + l % lpg -- so each lane loads the metadata of R/lpg rows, and
     // one combine and one fold serve lpg rows.  (Every instance uses this
@@ -596,9 +596,9 @@ void qmv_affine_kernel(const Params p)
     // does not own, which gives the same bits.  One vector keeps that form:
     // its short compute after the last load is latency-bound, and grouping
     // adds the per-word lane selects to it.)
-    constexpr bool PAIRED = !XF32 && (R % LPG == 0) && ((LPG == 2 && M >= 2) || (LPG == 4 && M >= 9));
-    constexpr int RS = PAIRED ? R / LPG : R;      // rows each lane folds (accumulator sets)
-    constexpr int SKIP = PAIRED ? (LPG == 4 ? 2 : 1) : 0;   // reduction levels inside a group
+    constexpr bool GROUPED = !XF32 && (R % LPG == 0) && ((LPG == 2 && M >= 2) || (LPG == 4 && M >= 9));
+    constexpr int RS = GROUPED ? R / LPG : R;      // rows each lane folds (accumulator sets)
+    constexpr int SKIP = GROUPED ? (LPG == 4 ? 2 : 1) : 0;   // reduction levels inside a group
     constexpr int V = RS * M;
     constexpr int P = pow2_at_least(V);
     static_assert(P <= (64 >> SKIP), "too many row totals per lane");
@@ -646,7 +646,7 @@ void qmv_affine_kernel(const Params p)
             i_sw[r] = rr * p.row_bytes;
             i_ss[r] = rr * p.G * 2;
         }
-        if constexpr (PAIRED) {
+        if constexpr (GROUPED) {
 #pragma unroll
             for (int k = 0; k < RS; ++k) i_ps[k] = min(k * LPG + lane % LPG, p.N - 1 - rbase) * p.G * 2;
         }
@@ -663,7 +663,7 @@ void qmv_affine_kernel(const Params p)
         for (int r = 0; r < R; ++r) wv[r] = buf_load_nt(i_wr, wo, i_sw[r]);
 #pragma unroll
         for (int k = 0; k < RS; ++k) {
-            if constexpr (PAIRED) {
+            if constexpr (GROUPED) {
                 sv[k] = buf_load_u16(i_sr, mo + i_ps[k], 0);
                 bv[k] = buf_load_u16(i_br, mo + i_ps[k], 0);
             } else {
@@ -687,7 +687,7 @@ void qmv_affine_kernel(const Params p)
     const uint32_t magic = opaque_u32(code_magic<BITS>());
     Stager<BITS, GS, M, XF32> stg;
     uint4 wb[NS][R];
-    unsigned short sb[NS][RS], bb[NS][RS];  // scale and bias bits (of the lane's own rows when paired)
+    unsigned short sb[NS][RS], bb[NS][RS];  // scale and bias bits (of the lane's own rows when grouped)
     auto prologue = [&]() {
 #pragma unroll
         for (int s = 0; s < PF; ++s) issue(wb[s], sb[s], bb[s]);
@@ -725,10 +725,10 @@ void qmv_affine_kernel(const Params p)
                 }
                 const uint4 (&wcur)[R] = wb[s];
                 // Scale and bias of each row's group.  The group's owner is the lane
-                // l with l % lpg == n % lpg for row n.  Unpaired, every lane folds
+                // l with l % lpg == n % lpg for row n.  Ungrouped, every lane folds
                 // every row with the scale and bias zeroed on all lanes but the
                 // owner, so the fold acc = s*D + (b*S + acc) leaves a non-owner's
-                // accumulator unchanged without a branch; paired, each lane loaded
+                // accumulator unchanged without a branch; grouped, each lane loaded
                 // only its own rows' values.
                 const int rb0 = (((int)blockIdx.x + c_rb * grid) * W + wave) * R;   // block's first row
                 float sv[RS], bv[RS];
@@ -736,7 +736,7 @@ void qmv_affine_kernel(const Params p)
                 for (int k = 0; k < RS; ++k) {
                     const float fs = SBF ? bf16_to_f32_here(sb[s][k]) : f16_to_f32_here(sb[s][k]);
                     const float fb = SBF ? bf16_to_f32_here(bb[s][k]) : f16_to_f32_here(bb[s][k]);
-                    if constexpr (PAIRED) {
+                    if constexpr (GROUPED) {
                         sv[k] = fs;
                         bv[k] = fb;
                     } else {
@@ -796,7 +796,7 @@ void qmv_affine_kernel(const Params p)
                         uint32_t w[LPG];
 #pragma unroll
                         for (int t = 0; t < LPG; ++t) {
-                            const uint4& wr = wcur[PAIRED ? LPG * k + t : 0];
+                            const uint4& wr = wcur[GROUPED ? LPG * k + t : 0];
                             w[t] = (i == 0) ? wr.x : (i == 1) ? wr.y : (i == 2) ? wr.z : wr.w;
                         }
                         const bool b0 = (lane & 1) != 0;
@@ -830,7 +830,7 @@ void qmv_affine_kernel(const Params p)
                         float S[M], c0[M];
 #pragma unroll
                         for (int m = 0; m < M; ++m) read_x(m, xo0, xp[m], S[m], c0[m]);
-                        if constexpr (PAIRED) {
+                        if constexpr (GROUPED) {
 #pragma unroll
                             for (int k = 0; k < RS; ++k) {
                                 float d[LPG][M];
@@ -910,7 +910,7 @@ void qmv_affine_kernel(const Params p)
                         };
                         read_xr(0, xo0, xq[0], Sq[0], cq[0]);
                         uint32_t qp[R][NP];
-                        if constexpr (PAIRED) {
+                        if constexpr (GROUPED) {
 #pragma unroll
                             for (int k = 0; k < RS; ++k) {
                                 uint32_t ws[4][LPG];
@@ -930,7 +930,7 @@ void qmv_affine_kernel(const Params p)
                                 const int xo = (m == 0) ? xo0 : after(xo0, acc[RS - 1][m - 1]);
                                 read_xr(m + 1, xo, xq[(m + 1) & 1], Sq[(m + 1) & 1], cq[(m + 1) & 1]);
                             }
-                            if constexpr (PAIRED) {
+                            if constexpr (GROUPED) {
                                 float d[R];
 #pragma unroll
                                 for (int r = 0; r < R; ++r) {
@@ -942,7 +942,7 @@ void qmv_affine_kernel(const Params p)
                                 for (int k = 0; k < RS; ++k) {
                                     float dv[LPG];
 #pragma unroll
-                                    for (int j = 0; j < LPG; ++j) dv[j] = d[PAIRED ? LPG * k + j : 0];
+                                    for (int j = 0; j < LPG; ++j) dv[j] = d[GROUPED ? LPG * k + j : 0];
                                     const float dd = combine(dv);
                                     acc[k][m] = pinned(__builtin_fmaf(sv[k], dd, __builtin_fmaf(bv[k], Sq[m & 1], acc[k][m])));
                                 }
@@ -1021,7 +1021,7 @@ void qmv_affine_kernel(const Params p)
                     lane_reduce<P, SKIP>(v, lane);
                     const int idx = reduce_index<P, SKIP>(lane);
                     const int k = idx / M, m = idx - (idx / M) * M;
-                    const int r = PAIRED ? LPG * k + lane % LPG : k;
+                    const int r = GROUPED ? LPG * k + lane % LPG : k;
                     const bool holder = ((lane >> SKIP) % ((64 >> SKIP) / P)) == 0;
                     if (holder && idx < V && rb0 + r < p.N) {
                         const size_t o = (size_t)m * p.N + rb0 + r;
