@@ -163,3 +163,19 @@ def test_graph_capture_replays_match_eager():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(_bits(y_graph), _bits(eager)), f"replay {i}"
+
+
+def test_lds_limit_kept_across_shapes():
+    # One kernel instance serves shapes with different LDS sizes above the
+    # 64 KiB default (fp32 activations, 4 vectors: two and three wave steps of
+    # K staged whole).  Planning the smaller one after the larger one must not
+    # lower the limit the larger one's launch needs.
+    infos = [U.q.kernel_info(4, 512, K, 4, 64, x_dt=U.q.DT_F32) for K in (6144, 4096)]
+    assert infos[0]["lds_bytes"] > infos[1]["lds_bytes"] > 65536, infos
+    assert infos[0]["k_windows"] == infos[1]["k_windows"] == 1
+    for K in (6144, 4096, 6144):
+        p = gen.make_problem(N=512, K=K, bits=4, gs=64, sb="bf16", x_dtype="f32", seed=K)
+        dev = U.to_dev(p)
+        U.say(f"LDS limit K={K}")
+        y = U.gpu(p, dev, 4, torch.float32)
+        U.check_parity(y, U.ref(p, 4), f"K={K}")
