@@ -179,3 +179,46 @@ def test_lds_limit_kept_across_shapes():
         U.say(f"LDS limit K={K}")
         y = U.gpu(p, dev, 4, torch.float32)
         U.check_parity(y, U.ref(p, 4), f"K={K}")
+
+
+def test_concurrent_calls_from_host_threads():
+    # Calls from several host threads, each on its own stream, with shapes and
+    # M that the first call of each thread still has to plan: every result
+    # equals the same call made alone.
+    import threading
+    probs = [gen.make_problem(N=N, K=K, bits=bits, gs=gs, sb="bf16", x_dtype="bf16", seed=N + K)
+             for N, K, bits, gs in ((300, 2560, 4, 64), (517, 1536, 4, 128), (260, 4096, 2, 128), (129, 1024, 2, 64))]
+    devs = [U.to_dev(p) for p in probs]
+    Ms = (1, 3, 7, 13)
+    jobs = [(i, M) for i in range(len(probs)) for M in Ms]
+    out = {}
+    errors = []
+
+    def worker(t):
+        try:
+            st = torch.cuda.Stream()
+            with torch.cuda.stream(st):
+                for k in range(3):
+                    for j, (i, M) in enumerate(jobs):
+                        if (j + t) % 4 == 0:
+                            w, s, b, x = devs[i]
+                            y = U.q.affine(w, s, b, x[:M], bits=probs[i].bits, group_size=probs[i].gs,
+                                           out_dtype=torch.float32)
+                            out[(t, k, i, M)] = y
+            st.synchronize()
+        except Exception as e:  # noqa: BLE001
+            errors.append(repr(e))
+
+    U.say("concurrent host threads")
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(4)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    assert not errors, errors
+    torch.cuda.synchronize()
+    for (t, k, i, M), y in out.items():
+        w, s, b, x = devs[i]
+        alone = U.gpu(probs[i], devs[i], M, torch.float32)
+        assert torch.equal(_bits(y), _bits(alone)), (t, k, i, M)
+    assert len(out) == 3 * len(jobs)
