@@ -26,9 +26,10 @@
 //     in one round).
 //     All activation loads are issued before the first weight load, and the
 //     weight prologue is in flight while the activations are converted.
-//   * Each lane loads the scale and bias of its own group: of every row (and
-//     zeroes them in registers where it does not own the group), or, with
-//     grouped rows (step 4 below), of the rows it owns.  Rows past N and chunks
+//   * Each lane loads the scale and bias of its own group, of the rows whose
+//     group it owns (step 4 below) when the rows per wavefront are a multiple
+//     of lpg, else of every row (zeroing them in registers where it does not
+//     own the group).  Rows past N and chunks
 //     past a row's end read clamped, in-bounds addresses; the activations,
 //     chain starts and group sums of chunks past the row's end are zero in
 //     LDS, so those lanes add nothing.
@@ -598,6 +599,11 @@ void qmv_affine_kernel(const Params p)
     // adds the per-word lane selects to it.)
     constexpr bool GROUPED = !XF32 && (R % LPG == 0) && ((LPG == 2 && M >= 2) || (LPG == 4 && M >= 9));
     constexpr int RS = GROUPED ? R / LPG : R;      // rows each lane folds (accumulator sets)
+    // Rows whose scale and bias a lane loads: with a multiple of lpg rows per
+    // wavefront a lane owns the groups of one row in lpg, in either form, so
+    // it loads only those rows' values (the rows lpg*k + l % lpg).
+    constexpr bool OWNLOAD = (LPG == 2 || LPG == 4) && (R % LPG == 0);
+    constexpr int RL = OWNLOAD ? R / LPG : R;
     constexpr int SKIP = GROUPED ? (LPG == 4 ? 2 : 1) : 0;   // reduction levels inside a group
     constexpr int V = RS * M;
     constexpr int P = pow2_at_least(V);
@@ -630,7 +636,7 @@ void qmv_affine_kernel(const Params p)
     const int row_step = grid * W * R;
     __amdgpu_buffer_rsrc_t i_wr, i_sr, i_br;
     int i_sw[R], i_ss[R];                            // per-row scalar offsets (weights, scales/biases)
-    int i_ps[RS];                                    // grouped: offset of the lane's own row of each row group
+    int i_ps[RL];                                    // offset of the lane's own row of each row group
     auto set_block = [&]() {
         // every input of the resources is wave-uniform; readfirstlane makes that
         // explicit (a resource the compiler cannot prove uniform costs a
@@ -646,9 +652,9 @@ void qmv_affine_kernel(const Params p)
             i_sw[r] = rr * p.row_bytes;
             i_ss[r] = rr * p.G * 2;
         }
-        if constexpr (GROUPED) {
+        if constexpr (OWNLOAD) {
 #pragma unroll
-            for (int k = 0; k < RS; ++k) i_ps[k] = min(k * LPG + lane % LPG, p.N - 1 - rbase) * p.G * 2;
+            for (int k = 0; k < RL; ++k) i_ps[k] = min(k * LPG + lane % LPG, p.N - 1 - rbase) * p.G * 2;
         }
     };
     set_block();
@@ -656,14 +662,14 @@ void qmv_affine_kernel(const Params p)
     const int mo0 = (lane / LPG) * 2;                // lane's group offset in a row's first step
     int i_wo = wo0, i_mo = mo0;
     const int wo_max = p.row_bytes - 16, mo_max = p.G * 2 - 2;
-    auto issue = [&](uint4 (&wv)[R], unsigned short (&sv)[RS], unsigned short (&bv)[RS]) {
+    auto issue = [&](uint4 (&wv)[R], unsigned short (&sv)[RL], unsigned short (&bv)[RL]) {
         const int wo = min(i_wo, wo_max);
         const int mo = min(i_mo, mo_max);
 #pragma unroll
         for (int r = 0; r < R; ++r) wv[r] = buf_load_nt(i_wr, wo, i_sw[r]);
 #pragma unroll
-        for (int k = 0; k < RS; ++k) {
-            if constexpr (GROUPED) {
+        for (int k = 0; k < RL; ++k) {
+            if constexpr (OWNLOAD) {
                 sv[k] = buf_load_u16(i_sr, mo + i_ps[k], 0);
                 bv[k] = buf_load_u16(i_br, mo + i_ps[k], 0);
             } else {
@@ -687,7 +693,7 @@ void qmv_affine_kernel(const Params p)
     const uint32_t magic = opaque_u32(code_magic<BITS>());
     Stager<BITS, GS, M, XF32> stg;
     uint4 wb[NS][R];
-    unsigned short sb[NS][RS], bb[NS][RS];  // scale and bias bits (of the lane's own rows when grouped)
+    unsigned short sb[NS][RL], bb[NS][RL];  // scale and bias bits (of the lane's own rows with OWNLOAD)
     auto prologue = [&]() {
 #pragma unroll
         for (int s = 0; s < PF; ++s) issue(wb[s], sb[s], bb[s]);
@@ -728,21 +734,32 @@ void qmv_affine_kernel(const Params p)
                 // l with l % lpg == n % lpg for row n.  Ungrouped, every lane folds
                 // every row with the scale and bias zeroed on all lanes but the
                 // owner, so the fold acc = s*D + (b*S + acc) leaves a non-owner's
-                // accumulator unchanged without a branch; grouped, each lane loaded
-                // only its own rows' values.
+                // accumulator unchanged without a branch; grouped, each lane folds
+                // only its own rows.  With a multiple of lpg rows per wavefront the
+                // block's first row is a multiple of lpg, so row r's owner is the
+                // lane with l % lpg == r % lpg, and a lane loaded only the values of
+                // the rows it owns.
                 const int rb0 = (((int)blockIdx.x + c_rb * grid) * W + wave) * R;   // block's first row
                 float sv[RS], bv[RS];
+                float fs[RL], fb[RL];
+#pragma unroll
+                for (int k = 0; k < RL; ++k) {
+                    fs[k] = SBF ? bf16_to_f32_here(sb[s][k]) : f16_to_f32_here(sb[s][k]);
+                    fb[k] = SBF ? bf16_to_f32_here(bb[s][k]) : f16_to_f32_here(bb[s][k]);
+                }
 #pragma unroll
                 for (int k = 0; k < RS; ++k) {
-                    const float fs = SBF ? bf16_to_f32_here(sb[s][k]) : f16_to_f32_here(sb[s][k]);
-                    const float fb = SBF ? bf16_to_f32_here(bb[s][k]) : f16_to_f32_here(bb[s][k]);
                     if constexpr (GROUPED) {
-                        sv[k] = fs;
-                        bv[k] = fb;
+                        sv[k] = fs[k];
+                        bv[k] = fb[k];
+                    } else if constexpr (OWNLOAD) {
+                        const bool own = (lane % LPG) == (k % LPG);
+                        sv[k] = own ? fs[k / LPG] : 0.0f;
+                        bv[k] = own ? fb[k / LPG] : 0.0f;
                     } else {
                         const bool own = (lane % LPG) == ((rb0 + k) % LPG);
-                        sv[k] = own ? fs : 0.0f;
-                        bv[k] = own ? fb : 0.0f;
+                        sv[k] = own ? fs[k] : 0.0f;
+                        bv[k] = own ? fb[k] : 0.0f;
                     }
                 }
                 const int xo0 = xl + c_tw * XSTEP;            // chunk's LDS offset (never straddles padding)
