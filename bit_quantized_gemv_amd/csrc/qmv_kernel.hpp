@@ -29,10 +29,9 @@
 //   * Each lane loads the scale and bias of its own group, of the rows whose
 //     group it owns (step 4 below) when the rows per wavefront are a multiple
 //     of lpg, else of every row (zeroing them in registers where it does not
-//     own the group).  Rows past N and chunks
-//     past a row's end read clamped, in-bounds addresses; the activations,
-//     chain starts and group sums of chunks past the row's end are zero in
-//     LDS, so those lanes add nothing.
+//     own the group).  Rows past N and chunks past a row's end read clamped,
+//     in-bounds addresses; the activations, chain starts and group sums of
+//     chunks past the row's end are zero in LDS, so those lanes add nothing.
 //   * The weight decode of a chunk happens once per step, outside the loop over
 //     the M vectors; every vector then reuses the decoded registers.
 //
