@@ -1,0 +1,48 @@
+"""GPU parity on a seeded sweep of random shapes and dtypes: ragged N, K from
+one group up, both code widths and group sizes, every activation / parameter
+/ output dtype, M up to 27 (several tiles of vectors) and forced rows per
+wavefront.  Each case is checked against the oracle, the bf16 output against
+the rounded fp32 output, and its first and last vector against one-vector
+calls bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+import gpu_util as U
+from inputs import gen
+
+pytestmark = pytest.mark.gpu
+
+
+def _cases(n=160, seed=2024):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        bits = int(rng.choice([2, 4]))
+        gs = int(rng.choice([64, 128]))
+        K = gs * int(rng.integers(1, 81))
+        N = int(rng.integers(1, 321))
+        sb = str(rng.choice(["f16", "bf16"]))
+        xdt = str(rng.choice(["f32", "bf16"]))
+        M = int(rng.choice([1, 2, 3, 4, 5, 7, 9, 13, 14, 20, 27]))
+        R = int(rng.choice([0, 0, 1, 2, 3, 4]))
+        out.append((N, K, bits, gs, sb, xdt, M, R, 3000 + i))
+    return out
+
+
+@pytest.mark.parametrize("case", _cases(),
+                         ids=lambda c: f"N{c[0]}_K{c[1]}_b{c[2]}_g{c[3]}_{c[4]}_{c[5]}_M{c[6]}_R{c[7]}")
+def test_random_shape_vs_oracle(case):
+    N, K, bits, gs, sb, xdt, M, R, seed = case
+    p = gen.make_problem(N=N, K=K, bits=bits, gs=gs, sb=sb, x_dtype=xdt, seed=seed)
+    dev = U.to_dev(p)
+    xs = gen.make_x(K, xdt, seed, rows=max(M, 13))
+    xd = U.x_to_dev(xs, xdt)
+    U.say(f"random N={N} K={K} bits={bits} gs={gs} sb={sb} x={xdt} M={M} R={R}")
+    y = U.gpu(p, dev, M, torch.float32, R=R, x=xd)
+    U.check_parity(y, U.ref(p, M, x=xs), f"N={N} K={K} M={M}")
+    y16 = U.gpu(p, dev, M, torch.bfloat16, R=R, x=xd)
+    assert torch.equal(y16.view(torch.int16), U.rne_bf16(y).view(torch.int16))
+    for m in sorted({0, M - 1}):
+        one = U.gpu(p, dev, 1, torch.float32, R=R, x=xd[m:m + 1])
+        assert torch.equal(y[m].view(torch.int32), one[0].view(torch.int32)), f"vector {m}"
