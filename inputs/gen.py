@@ -88,6 +88,32 @@ def make_weights(N: int, K: int, bits: int, gs: int, sb: str, seed: int, keep_q:
     return w, _bits16(scale), _bits16(bias), (qn if keep_q else None)
 
 
+@dataclass
+class MxProblem:
+    """The mxfp4 mode: E2M1 codes packed 8 per uint32 (field 0 low), one E8M0
+    scale byte per block of 32 along K."""
+    N: int
+    K: int
+    x_dtype: str
+    w_packed: np.ndarray  # uint32 [N][K/8]
+    scales: np.ndarray    # uint8 [N][K/32]
+    x: np.ndarray         # float32 [13][K] or uint16 bf16 bit patterns [13][K]
+    q: np.ndarray | None = field(default=None, repr=False)  # uint8 [N][K] codes (optional)
+
+
+def make_mx_problem(N: int, K: int, x_dtype: str = "bf16", seed: int = 0, keep_q: bool = False,
+                    e_lo: int = 116, e_hi: int = 124) -> MxProblem:
+    """Uniform random E2M1 codes (both signs, every magnitude) and block scale
+    exponents uniform in [e_lo, e_hi] -- 2^-11 .. 2^-3 around 127, the scales
+    a 0.02-wide weight distribution gets when its block maximum maps near the
+    E2M1 maximum of 6."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    q = torch.randint(0, 16, (N, K), generator=g, dtype=torch.uint8).numpy()
+    e = torch.randint(e_lo, e_hi + 1, (N, K // 32), generator=g, dtype=torch.int32).numpy().astype(np.uint8)
+    return MxProblem(N=N, K=K, x_dtype=x_dtype, w_packed=pack(q, 4), scales=e,
+                     x=make_x(K, x_dtype, seed), q=(q if keep_q else None))
+
+
 def make_x(K: int, x_dtype: str, seed: int, rows: int = MAX_M) -> np.ndarray:
     g = torch.Generator("cpu").manual_seed(seed + 500)
     x = torch.randn(rows, K, generator=g)

@@ -1,4 +1,5 @@
-"""Python access to the plain C oracle of the affine group-quantized qmv.
+"""Python access to the plain C oracle of the affine group-quantized qmv (and
+of its mxfp4 mode).
 
 TEST INFRASTRUCTURE ONLY: imported by tests/, by __graft_entry__.smoke() and by
 the cpu_baseline leg of bench.py.  The GPU package never imports this module.
@@ -67,6 +68,12 @@ class Oracle:
         L.orc_round_outputs.restype = None
         L.orc_max_threads.argtypes = []
         L.orc_max_threads.restype = I
+        L.orc_qmv_mxfp4.argtypes = [P, P, P, I, P, I, I, I, I]
+        L.orc_qmv_mxfp4.restype = I
+        L.orc_e2m1_to_f64.argtypes = [ctypes.c_uint]
+        L.orc_e2m1_to_f64.restype = ctypes.c_double
+        L.orc_e8m0_to_f64.argtypes = [ctypes.c_uint]
+        L.orc_e8m0_to_f64.restype = ctypes.c_double
         self.L = L
 
     def qmv(self, w_packed, scales, biases, x, *, bits, group_size, sb_dtype, x_dtype,
@@ -109,6 +116,32 @@ class Oracle:
         if rc != 0:
             raise ValueError(f"oracle rejected the request (code {rc})")
         return out
+
+    def qmv_mxfp4(self, w_packed, scales, x, *, x_dtype, nthreads: int = 0) -> np.ndarray:
+        """y_ref[M][N] (float64) of the mxfp4 mode.
+
+        w_packed: uint32 [N][K/8] (E2M1 codes, field 0 low); scales: uint8
+        [N][K/32] (E8M0); x: float32 [M][K] (x_dtype F32) or uint16 bf16 bit
+        patterns [M][K] (x_dtype BF16).
+        """
+        w_packed = np.ascontiguousarray(w_packed, dtype=np.uint32)
+        scales = np.ascontiguousarray(scales, dtype=np.uint8)
+        x = np.ascontiguousarray(x, dtype=np.float32 if x_dtype == F32 else np.uint16)
+        N = w_packed.shape[0]
+        M, K = x.shape
+        assert w_packed.shape[1] * 8 == K and scales.shape == (N, K // 32)
+        y = np.zeros((M, N), dtype=np.float64)
+        rc = self.L.orc_qmv_mxfp4(_ptr(w_packed), _ptr(scales), _ptr(x), x_dtype, _ptr(y),
+                                  M, N, K, nthreads)
+        if rc != 0:
+            raise ValueError(f"oracle rejected the shape (code {rc})")
+        return y
+
+    def e2m1_to_f64(self, c: int) -> float:
+        return self.L.orc_e2m1_to_f64(c)
+
+    def e8m0_to_f64(self, e: int) -> float:
+        return self.L.orc_e8m0_to_f64(e)
 
     def unpack_row(self, row, K: int, bits: int) -> np.ndarray:
         row = np.ascontiguousarray(row, dtype=np.uint32)

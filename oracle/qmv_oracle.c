@@ -8,7 +8,7 @@
  * table or helper with the GPU path.
  *
  * What it computes (fp64 accumulation, no blocking, no reordering beyond the
- * grouped definition itself):
+ * grouped definition itself; the mxfp4 mode further below):
  *
  *   y[m][n] = sum_g ( scale[n][g] * sum_{k in g} q[n][k] * x[m][k]
  *                   + bias[n][g]  * sum_{k in g} x[m][k] )
@@ -174,6 +174,69 @@ int orc_qmv_affine_at(const uint32_t* w, const void* scales, const void* biases,
     #pragma omp parallel for schedule(static)
     for (int i = 0; i < count; ++i)
         out[i] = one(w, scales, biases, sb_dt, x, x_dt, ms[i], ns[i], K, bits, gs);
+    return 0;
+}
+
+/* ------------------------------------------------------------------ mxfp4
+ * Microscaling FP4 (the "mxfp4" quantization mode the MLX pages list beside
+ * the affine one; the pages do not define it, so the definition is the OCP
+ * Microscaling Formats (MX) specification v1.0): blocks of 32 elements share
+ * one E8M0 scale X = 2^(E - 127) (E = 255 encodes NaN); each element is FP4
+ * E2M1 -- sign bit 3, exponent bits 2..1 with bias 1, mantissa bit 0;
+ * exponent 0 is the subnormal range, 2^(1-1) * (m / 2); no inf or NaN.
+ * Elements are packed 8 per uint32 with field 0 in the low bits (the affine
+ * 4-bit packing), scales are uint8 [N][K/32]:
+ *
+ *   y[m][n] = sum_b X[n][b] * sum_{k in b} e2m1(q[n][k]) * x[m][k]
+ *
+ * Every element, scale and activation converts to double exactly, and each
+ * product is exact in double.
+ */
+double orc_e2m1_to_f64(unsigned c)
+{
+    int sign = (c >> 3) & 1;
+    int e = (c >> 1) & 3;
+    int m = c & 1;
+    double v = (e == 0) ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+    return sign ? -v : v;
+}
+
+double orc_e8m0_to_f64(unsigned E)
+{
+    return (E & 0xffu) == 0xffu ? NAN : ldexp(1.0, (int)(E & 0xffu) - 127);
+}
+
+static double one_mx(const uint32_t* w, const uint8_t* scales, const void* x, int x_dt,
+                     int m, int n, int K)
+{
+    const int B = K / 32;
+    const uint32_t* row = w + (size_t)n * (size_t)(K / 8);
+    double acc = 0.0;
+    for (int b = 0; b < B; ++b) {
+        double D = 0.0;
+        for (int k = b * 32; k < (b + 1) * 32; ++k)
+            D += orc_e2m1_to_f64(orc_field(row, k, 4)) *
+                 elem(x, (size_t)m * (size_t)K + (size_t)k, x_dt);
+        acc += orc_e8m0_to_f64(scales[(size_t)n * B + b]) * D;
+    }
+    return acc;
+}
+
+/* y[m*N + n] (double) for all m < M, n < N; K a multiple of 32. */
+int orc_qmv_mxfp4(const uint32_t* w, const uint8_t* scales, const void* x, int x_dt,
+                  double* y, int M, int N, int K, int nthreads)
+{
+    if (M < 0 || N < 0 || K < 0) return -3;
+    if (K % 32) return -4;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+    #pragma omp parallel for schedule(static)
+    for (int n = 0; n < N; ++n)
+        for (int m = 0; m < M; ++m)
+            y[(size_t)m * N + n] = one_mx(w, scales, x, x_dt, m, n, K);
     return 0;
 }
 

@@ -300,6 +300,59 @@ def pin_sampled_matches_full(orc):
     assert np.array_equal(z, y[ms, ns])
 
 
+# ------------------------------------------------------------- mxfp4 mode ---
+
+def _mx_golden():
+    with open(os.path.join(GOLDEN, "mxfp4_e2m1.json")) as f:
+        return json.load(f)
+
+
+def pin_mx_codes_golden(orc):
+    """Every E2M1 code and sample E8M0 scales against hand-worked values."""
+    gd = _mx_golden()
+    for c, v in enumerate(gd["e2m1"]):
+        got = orc.e2m1_to_f64(c)
+        assert got == v and np.signbit(got) == np.signbit(v), (c, got, v)
+    for e, v in gd["e8m0"]:
+        assert orc.e8m0_to_f64(e) == v, (e, orc.e8m0_to_f64(e), v)
+    assert np.isnan(orc.e8m0_to_f64(gd["e8m0_nan"]))
+
+
+def _mx_dense(p):
+    """Dequantized weights from numpy bit unpacking, the golden code table and
+    ldexp of the scale bytes: W[n][k] = 2^(E[n][k/32] - 127) * e2m1(q[n][k])."""
+    table = np.array(_mx_golden()["e2m1"], dtype=np.float64)
+    q = decode_unpackbits(p.w_packed, 4)
+    sc = np.ldexp(1.0, p.scales.astype(np.int64) - 127)
+    return table[q] * np.repeat(sc, 32, axis=1)
+
+
+def pin_mx_bruteforce(orc):
+    """Dequantize-then-dot (numpy matmul over the dense weights) equals the
+    oracle's blocked form to fp64 rounding, on several tiny shapes."""
+    for N, K, xdt, seed in ((7, 96, "bf16", 1), (5, 32, "f32", 2), (11, 256, "bf16", 3)):
+        p = gen.make_mx_problem(N, K, xdt, seed, e_lo=100, e_hi=140)
+        x64 = x_to_f64(p.x[:3], xdt)
+        want = x64 @ _mx_dense(p).T
+        got = orc.qmv_mxfp4(p.w_packed, p.scales, p.x[:3], x_dtype=F32 if xdt == "f32" else BF16)
+        assert normwise(got, want) <= 1e-12, (N, K, normwise(got, want))
+
+
+def pin_mx_readout(orc):
+    """Scale 1 (E = 127) and x = e_k read one code value back exactly; a
+    scale byte one higher doubles it exactly."""
+    table = np.array(_mx_golden()["e2m1"], dtype=np.float64)
+    p = gen.make_mx_problem(9, 128, "f32", 4, keep_q=True)
+    ks = [0, 1, 7, 8, 31, 32, 63, 64, 100, 127]
+    x = np.zeros((len(ks), 128), dtype=np.float32)
+    x[np.arange(len(ks)), ks] = 1.0
+    for E, mult in ((127, 1.0), (128, 2.0)):
+        sc = np.full(p.scales.shape, E, dtype=np.uint8)
+        y = orc.qmv_mxfp4(p.w_packed, sc, x, x_dtype=F32)
+        assert np.array_equal(y, mult * table[p.q[:, ks].T]), E
+
+
 ALL_PINS = [pin_codec_golden, pin_2bit_float_floor_exhaustive, pin_4bit_nibbles_exhaustive,
             pin_readout, pin_worked_examples, pin_bruteforce_dequant, pin_closed_forms,
-            pin_conversions, pin_sampled_matches_full]
+            pin_conversions, pin_sampled_matches_full,
+            pin_mx_codes_golden, pin_mx_bruteforce, pin_mx_readout]

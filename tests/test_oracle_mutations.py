@@ -27,6 +27,14 @@ MUTANTS = {
     "f16_subnormal_flushed": ("v = ldexp((double)f, -24);", "v = 0.0;"),
     "bf16_ties_away": ("(lower == 0x8000u && (upper & 1u))", "(lower == 0x8000u)"),
     "row_stride_wrong": ("(size_t)n * (size_t)(K * bits / 32)", "(size_t)n * (size_t)(K * bits / 32 - 1)"),
+    # mxfp4 mode
+    "e2m1_exponent_bias": ("ldexp(1.0 + 0.5 * m, e - 1)", "ldexp(1.0 + 0.5 * m, e)"),
+    "e2m1_subnormal": ("(e == 0) ? 0.5 * m :", "(e == 0) ? 1.0 * m :"),
+    "e2m1_sign_ignored": ("ldexp(1.0 + 0.5 * m, e - 1);\n    return sign ? -v : v;",
+                          "ldexp(1.0 + 0.5 * m, e - 1);\n    return v;"),
+    "e8m0_bias": ("(int)(E & 0xffu) - 127", "(int)(E & 0xffu) - 126"),
+    "mx_block_scale_shifted": ("scales[(size_t)n * B + b]", "scales[(size_t)n * B + (b + 1) % B]"),
+    "mx_block_short": ("for (int k = b * 32; k < (b + 1) * 32; ++k)", "for (int k = b * 32; k < (b + 1) * 32 - 1; ++k)"),
 }
 
 
