@@ -1,0 +1,342 @@
+// qmv_mx.hip -- gfx950 kernel and C ABI of the mxfp4 mode of the streamed qmv:
+//
+//   y[m][n] = sum_b X[n][b] * sum_{k in b} e2m1(q[n][k]) * x[m][k]
+//
+// with FP4 E2M1 codes q packed 8 per uint32 (field 0 in the low bits), one
+// E8M0 scale X = 2^(E - 127) per block of 32 values along K, and bf16
+// activations.  The MLX pages list this quantization mode beside the affine
+// one (mlxcel issue "an order-preserving streamed qmv would give MTP the fast
+// kernel and byte-identity together", section "Scope limits") without
+// defining the format; the element and scale formats are those of the OCP
+// Microscaling Formats (MX) specification v1.0.
+//
+// Work decomposition and order (the affine kernel's, without bias and with
+// one block per lane):
+//   * Chunk c (16 bytes = 32 codes = one block) of a row is read by lane c % 64
+//     in wave step c / 64; a wavefront owns R consecutive rows; a workgroup of
+//     W wavefronts stages x[0..M)[0..K) in LDS (bf16, natural order, zero past
+//     the row's last chunk) and walks row blocks of W*R rows.
+//   * Per row, chunk and vector: the codes of each byte become an exact bf16
+//     pair (v_cvt_scalef32_pk_bf16_fp4 with scale 1: low nibble first); D is
+//     the v_dot2_f32_bf16 chain over the chunk's 16 pairs, in byte order,
+//     from 0; the lane folds acc = fma(X, D, acc) over its chunks in
+//     ascending step.  A lane owns its chunk's block, so no lanes combine.
+//   * Row total: lanes l and l ^ d combined for d = 32, 16, 8, 4, 2, 1, then
+//     round-to-nearest-even to y's dtype.
+//   None of this depends on M, R, W or the grid, so every output vector equals
+//   the one-vector call on that vector bit for bit.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+#include <mutex>
+#include <utility>
+
+#include "qmv.h"
+#include "qmv_kernel.hpp"
+
+namespace qmv {
+
+struct MxParams {
+    const uint32_t* w;
+    const uint8_t* s;
+    const uint16_t* x;
+    void* y;
+    int N;
+    int K;
+    int chunks;      // K / 32
+    int nsteps;      // ceil(chunks / 64)
+    int row_bytes;   // K / 2
+    int n_rb;        // row blocks of W*R rows
+    int y_bf16;
+    int xm_bytes;    // LDS bytes of one vector (nsteps*64 chunks of 64 B, padded)
+};
+
+// 2^(E - 127) as fp32 from an E8M0 byte: E = 0 is the subnormal 2^-127 and
+// E = 255 is NaN.
+__device__ __forceinline__ float e8m0_to_f32(uint32_t e)
+{
+    const uint32_t bits = (e == 0u) ? 0x00400000u : ((e == 255u) ? 0x7fc00000u : (e << 23));
+    return __uint_as_float(bits);
+}
+
+// The four bytes of a word of E2M1 codes as exact bf16 pairs, byte j ->
+// (code 2j, code 2j+1) with the low nibble in the low half (the byte select of
+// the conversion must be a constant).
+__device__ __forceinline__ uint4 fp4_word_to_bf16_pairs(uint32_t w)
+{
+    return make_uint4(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 0)),
+                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 1)),
+                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 2)),
+                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 3)));
+}
+
+template <int R, int M>
+__global__ __launch_bounds__(kMaxWaves * kWave) void qmv_mx_kernel(MxParams p)
+{
+    constexpr int V = R * M;
+    constexpr int P = pow2_at_least(V);
+    static_assert(P <= kWave, "too many row totals per lane");
+    extern __shared__ __align__(16) uint8_t lds[];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+    const int W = blockDim.x / kWave;
+    const int grid = gridDim.x;
+    if ((int)blockIdx.x >= p.n_rb) return;
+
+    // ---- stage x: 16-byte pieces, four per chunk; pieces of chunks past the
+    // row's end are zero.  All of a thread's loads are issued before any store.
+    {
+        const int cpad = p.nsteps * kWave;
+        const int items = M * cpad * 4;
+        const __amdgpu_buffer_rsrc_t xr = make_rsrc(p.x, M * p.K * 2);
+        for (int i0 = 0; i0 < items; i0 += 8 * (int)blockDim.x) {
+            uint4 v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int i = min(i0 + j * (int)blockDim.x + (int)threadIdx.x, items - 1);
+                const int m = i / (cpad * 4), rem = i - m * (cpad * 4);
+                const int c = min(rem >> 2, p.chunks - 1), piece = rem & 3;
+                v[j] = buf_load(xr, (m * p.K + c * 32 + piece * 8) * 2);
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int i = i0 + j * (int)blockDim.x + (int)threadIdx.x;
+                if (i < items) {
+                    const int m = i / (cpad * 4), rem = i - m * (cpad * 4);
+                    const int c = rem >> 2, piece = rem & 3;
+                    const uint4 d = (c < p.chunks) ? v[j] : make_uint4(0, 0, 0, 0);
+                    *reinterpret_cast<uint4*>(lds + m * p.xm_bytes + lds_phys(c * 64 + piece * 16)) = d;
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(p.w, -1);
+    const __amdgpu_buffer_rsrc_t sr = make_rsrc(p.s, -1);
+    for (int rb = blockIdx.x; rb < p.n_rb; rb += grid) {
+        const int n0 = (rb * W + wave) * R;
+        int roff[R], soff[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int n = min(n0 + r, p.N - 1);
+            roff[r] = n * p.row_bytes;
+            soff[r] = n * p.chunks;
+        }
+        float acc[R][M];
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
+
+        uint4 wb[2][R];
+        uint32_t eb[2][R];
+        auto issue = [&](int slot, int t) {
+            const int c = min(t * kWave + lane, p.chunks - 1);
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                wb[slot][r] = buf_load_nt(wr, roff[r] + c * 16, 0);
+                eb[slot][r] = __builtin_amdgcn_raw_buffer_load_b8(sr, soff[r] + c, 0, 0);
+            }
+        };
+        // one step: the next step's loads go out, then this step's chunk is
+        // decoded and every vector's chain and fold run (the slot is a
+        // compile-time constant, so the ring stays in registers)
+        auto step = [&](auto slot_tag, int t) {
+            constexpr int slot = decltype(slot_tag)::value;
+            issue(slot ^ 1, min(t + 1, p.nsteps - 1));
+            __builtin_amdgcn_sched_barrier(0);
+            const int c = t * kWave + lane;
+            uint32_t pr[R][16];
+            float sc[R];
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const uint32_t wd[4] = {wb[slot][r].x, wb[slot][r].y, wb[slot][r].z, wb[slot][r].w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint4 q4 = fp4_word_to_bf16_pairs(wd[i]);
+                    pr[r][4 * i] = q4.x;
+                    pr[r][4 * i + 1] = q4.y;
+                    pr[r][4 * i + 2] = q4.z;
+                    pr[r][4 * i + 3] = q4.w;
+                }
+                sc[r] = e8m0_to_f32(eb[slot][r] & 0xffu);
+            }
+            const uint8_t* xs = lds + lds_phys(c * 64);
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                uint32_t xp[16];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint4 q = *reinterpret_cast<const uint4*>(xs + m * p.xm_bytes + 16 * i);
+                    xp[4 * i] = q.x;
+                    xp[4 * i + 1] = q.y;
+                    xp[4 * i + 2] = q.z;
+                    xp[4 * i + 3] = q.w;
+                }
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    float d = 0.0f;
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) d = dot2(pr[r][i], xp[i], d);
+                    acc[r][m] = pinned(__builtin_fmaf(sc[r], d, acc[r][m]));
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        issue(0, 0);
+        for (int t = 0; t < p.nsteps; t += 2) {
+            step(std::integral_constant<int, 0>{}, t);
+            if (t + 1 < p.nsteps) step(std::integral_constant<int, 1>{}, t + 1);
+        }
+
+        // row totals: lane l ends with value reduce_index<P>(l)
+        float v[P];
+#pragma unroll
+        for (int i = 0; i < P; ++i) v[i] = (i < V) ? acc[i / M][i % M] : 0.0f;
+        lane_reduce<P>(v, lane);
+        const int idx = reduce_index<P>(lane);
+        const bool holder = (lane % (kWave / P)) == 0;
+        if (holder && idx < V) {
+            const int r = idx / M, m = idx - (idx / M) * M;
+            if (n0 + r < p.N) {
+                const size_t o = (size_t)m * p.N + n0 + r;
+                if (p.y_bf16)
+                    static_cast<uint16_t*>(p.y)[o] = (uint16_t)f32_to_bf16_rne(v[0]);
+                else
+                    static_cast<float*>(p.y)[o] = v[0];
+            }
+        }
+    }
+}
+
+}  // namespace qmv
+
+namespace {
+
+using MxKernelFn = void (*)(qmv::MxParams);
+
+template <int R, int... Ms>
+constexpr MxKernelFn mx_pick(int M, std::integer_sequence<int, Ms...>)
+{
+    MxKernelFn f = nullptr;
+    ((f = (M == Ms + 1) ? &qmv::qmv_mx_kernel<R, Ms + 1> : f), ...);
+    return f;
+}
+
+MxKernelFn mx_kernel(int R, int M)
+{
+    const auto seq = std::make_integer_sequence<int, QMV_TILE_M>{};
+    return R == 2 ? mx_pick<2>(M, seq) : mx_pick<4>(M, seq);
+}
+
+constexpr int kMxW = 8;                      // wavefronts per workgroup
+constexpr int kMxLds = 160 * 1024;
+
+bool overlap_mx(const void* a, size_t na, const void* b, size_t nb)
+{
+    const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+    return pa < pb + nb && pb < pa + na;
+}
+
+int mx_xm_bytes(int K)
+{
+    const int nsteps = (K / 32 + qmv::kWave - 1) / qmv::kWave;
+    return nsteps * qmv::kWave * 64 * 17 / 16;   // 16 bytes of padding per 256
+}
+
+// vectors per launch: at most QMV_TILE_M, and as many as fit in LDS whole
+int mx_vectors_per_launch(int K)
+{
+    return std::min(QMV_TILE_M, kMxLds / mx_xm_bytes(K));
+}
+
+std::mutex g_mx_mu;
+struct MxOcc {
+    MxKernelFn fn;
+    int dev, lds, blocks;
+};
+MxOcc g_mx_occ[256];
+int g_mx_nocc = 0;
+
+int mx_resident(MxKernelFn fn, int dev, int lds)
+{
+    std::lock_guard<std::mutex> lk(g_mx_mu);
+    for (int i = 0; i < g_mx_nocc; ++i)
+        if (g_mx_occ[i].fn == fn && g_mx_occ[i].dev == dev && g_mx_occ[i].lds == lds) return g_mx_occ[i].blocks;
+    const void* f = reinterpret_cast<const void*>(fn);
+    if (hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kMxLds) != hipSuccess) return -1;
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, f, kMxW * qmv::kWave, lds) != hipSuccess) return -1;
+    if (g_mx_nocc < 256) g_mx_occ[g_mx_nocc++] = MxOcc{fn, dev, lds, nb};
+    return nb;
+}
+
+int mx_check(const uint32_t* w, const uint8_t* s, const void* x, void* y, int M, int N, int K,
+             int y_dt)
+{
+    if (!w || !s || !x || !y) return QMV_E_NULL;
+    if (M < 1 || M > QMV_MAX_M) return QMV_E_M_RANGE;
+    if (N < 1 || N > QMV_MAX_N || K < 32 || K % 32 != 0 || K > QMV_MX_MAX_K) return QMV_E_SHAPE;
+    if (y_dt != QMV_DT_F32 && y_dt != QMV_DT_BF16) return QMV_E_DTYPE;
+    const size_t yb = (y_dt == QMV_DT_F32) ? 4 : 2;
+    if ((reinterpret_cast<uintptr_t>(w) % 16) || (reinterpret_cast<uintptr_t>(x) % 16) ||
+        (reinterpret_cast<uintptr_t>(y) % yb))
+        return QMV_E_ALIGN;
+    const size_t nw = (size_t)N * (size_t)K / 2, ns = (size_t)N * (size_t)(K / 32);
+    const size_t nx = (size_t)M * (size_t)K * 2, ny = (size_t)M * (size_t)N * yb;
+    if (overlap_mx(y, ny, w, nw) || overlap_mx(y, ny, s, ns) || overlap_mx(y, ny, x, nx))
+        return QMV_E_ALIAS;
+    return QMV_OK;
+}
+
+}  // namespace
+
+extern "C" int qmv_mxfp4(const uint32_t* w_packed, const uint8_t* scales, const void* x, void* y,
+                         int M, int N, int K, qmv_dtype y_dt, void* stream)
+{
+    const int st = mx_check(w_packed, scales, x, y, M, N, K, (int)y_dt);
+    if (st != QMV_OK) return st;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return QMV_E_LAUNCH;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        return QMV_E_LAUNCH;
+    const size_t yb = (y_dt == QMV_DT_F32) ? 4 : 2;
+    const int per_launch = mx_vectors_per_launch(K);
+    const int tiles = (M + per_launch - 1) / per_launch;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int m0 = 0;
+    for (int t = 0; t < tiles; ++t) {
+        // balanced tiles: the first M % tiles get one more vector
+        const int Mt = M / tiles + (t < M % tiles ? 1 : 0);
+        const int R = (Mt <= 2) ? 2 : 4;
+        const MxKernelFn fn = mx_kernel(R, Mt);
+        if (!fn) return QMV_E_LAUNCH;
+        qmv::MxParams p;
+        p.w = w_packed;
+        p.s = scales;
+        p.x = static_cast<const uint16_t*>(x) + (size_t)m0 * K;
+        p.y = static_cast<uint8_t*>(y) + (size_t)m0 * N * yb;
+        p.N = N;
+        p.K = K;
+        p.chunks = K / 32;
+        p.nsteps = (p.chunks + qmv::kWave - 1) / qmv::kWave;
+        p.row_bytes = K / 2;
+        p.n_rb = (N + kMxW * R - 1) / (kMxW * R);
+        p.y_bf16 = (y_dt == QMV_DT_BF16) ? 1 : 0;
+        p.xm_bytes = mx_xm_bytes(K);
+        const int lds = Mt * p.xm_bytes;
+        const int nb = mx_resident(fn, dev, lds);
+        if (nb <= 0) return QMV_E_LAUNCH;
+        const int grid = std::min(p.n_rb, nb * cus);
+        // the kernel's row offsets are 32-bit
+        if ((size_t)N * (size_t)p.row_bytes >= (size_t)1 << 31) return QMV_E_SHAPE;
+        void* args[] = {&p};
+        if (hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3(grid), dim3(kMxW * qmv::kWave), args,
+                            (size_t)lds, s) != hipSuccess)
+            return QMV_E_LAUNCH;
+        m0 += Mt;
+    }
+    return QMV_OK;
+}

@@ -155,6 +155,37 @@ int qmv_kernel_info(int M, int N, int K, int bits, int group_size, qmv_dtype x_d
  * QMV_E_LAUNCH on bad arguments or a refused launch. */
 int qmv_stream_read(const void* buf, long long bytes, uint32_t* out, int checksum, void* stream);
 
+/*
+ * mxfp4 mode: y = qmv(x) with FP4 (E2M1) codes and one E8M0 scale per block of
+ * 32 values along K, no bias:
+ *
+ *   y[m][n] = sum_b 2^(E[n][b] - 127) * sum_{k in b} e2m1(q[n][k]) * x[m][k]
+ *
+ * The MLX pages list this quantization mode beside the affine one (mlxcel
+ * issue "an order-preserving streamed qmv would give MTP the fast kernel and
+ * byte-identity together", section "Scope limits") without defining it; the
+ * element and scale formats are those of the OCP Microscaling Formats (MX)
+ * specification v1.0: E2M1 is sign bit 3, exponent bits 2..1 (bias 1),
+ * mantissa bit 0, exponent 0 subnormal (values 0, 0.5, 1, 1.5, 2, 3, 4, 6 and
+ * their negatives); E8M0 is 2^(E - 127), E = 255 NaN.
+ *   w_packed  uint32 [N][K/8], code k of a row in field k % 8 (bits
+ *             [4*(k%8), 4*(k%8)+4)) of word k / 8 -- field 0 in the low bits.
+ *   scales    uint8 [N][K/32] (E8M0), no alignment requirement.
+ *   x         bf16 [M][K]; y [M][N] of y_dt (QMV_DT_F32 or QMV_DT_BF16, RNE).
+ *   M in [1, QMV_MAX_M]; N in [1, QMV_MAX_N]; K a multiple of 32 in
+ *   [32, QMV_MX_MAX_K] with N*K/2 < 2^31; w_packed and x 16-byte aligned, y
+ *   aligned to its element size; y must not overlap an input.
+ * Numerics: each block's dot is an fp32 v_dot2 chain over its exact bf16 code
+ * pairs in K order, folded once as acc = fma(2^(E-127), D, acc) in ascending
+ * block order per lane, then a fixed 64-lane butterfly; every output vector
+ * equals the one-vector call on that vector bit for bit.  Ownership, streams
+ * and errors as for qmv_affine; at most QMV_TILE_M vectors per launch, fewer
+ * when K is long (x is staged in LDS whole), more run as balanced tiles.
+ */
+#define QMV_MX_MAX_K 65536
+int qmv_mxfp4(const uint32_t* w_packed, const uint8_t* scales, const void* x, void* y,
+              int M, int N, int K, qmv_dtype y_dt, void* stream);
+
 /* Static string naming a status code ("QMV_OK", "QMV_E_BITS", ...). */
 const char* qmv_status_string(int status);
 

@@ -13,7 +13,7 @@ HEADER = os.path.join(ROOT, "include", "qmv.h")
 def declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(qmv_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(qmv_[a-z0-9_]+)\s*\(", src)))
 
 
 @pytest.fixture(scope="module")
@@ -26,7 +26,7 @@ def L():
 
 
 def test_header_declares_the_boundary():
-    assert declared_functions() == ["qmv_affine", "qmv_affine_ex", "qmv_kernel_info",
+    assert declared_functions() == ["qmv_affine", "qmv_affine_ex", "qmv_kernel_info", "qmv_mxfp4",
                                     "qmv_status_string", "qmv_stream_read"]
 
 
@@ -106,3 +106,20 @@ def test_stream_read_validates(L):
     assert L.qmv_stream_read(4096, 0, 8192, 0, None) == 4
     assert L.qmv_stream_read(4104, 1024, 8192, 0, None) == 6          # QMV_E_ALIGN
     assert L.qmv_stream_read(4096, 1024, 8194, 0, None) == 6
+
+
+def test_mxfp4_validates(L):
+    # argument errors of the mxfp4 mode return before any HIP call
+    P, I = ctypes.c_void_p, ctypes.c_int
+    L.qmv_mxfp4.argtypes = [P, P, P, P, I, I, I, I, P]
+    w, s, x, y = 1 << 20, 1 << 24, 1 << 28, 1 << 32
+    F32, F16, BF16 = 0, 1, 2
+    call = lambda **k: L.qmv_mxfp4(k.get("w", w), k.get("s", s), k.get("x", x), k.get("y", y),
+                                   k.get("M", 1), k.get("N", 8), k.get("K", 64), k.get("dt", BF16), None)
+    assert call(w=None) == 1 and call(s=None) == 1 and call(x=None) == 1 and call(y=None) == 1
+    assert call(M=0) == 5 and call(M=65537) == 5                        # QMV_E_M_RANGE
+    assert call(K=48) == 4 and call(K=16) == 4 and call(K=65536 + 32) == 4 and call(N=0) == 4
+    assert call(dt=F16) == 7                                            # QMV_E_DTYPE
+    assert call(w=w + 8) == 6 and call(x=x + 8) == 6 and call(y=y + 2, dt=F32) == 6
+    assert call(y=w + 64) == 9                                          # QMV_E_ALIAS
+    assert call(s=s + 1) != 6                                           # scales need no alignment

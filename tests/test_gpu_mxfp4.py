@@ -1,0 +1,91 @@
+"""GPU parity of the mxfp4 mode through the C ABI against the oracle: small
+shapes over wave-step tails and ragged row blocks, the longest K, tiles of
+vectors, the up-projection workload, exact read-out, bf16 rounding, and every
+output vector against the one-vector call bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+import gpu_util as U
+from inputs import gen
+from oracle import oracle
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev(p):
+    w = torch.from_numpy(p.w_packed.view(np.int32)).to(U.DEV)
+    s = torch.from_numpy(p.scales).to(U.DEV)
+    return w, s
+
+
+def _x(p, rows):
+    xs = gen.make_x(p.K, "bf16", 7 + p.N, rows=rows)
+    return xs, U.x_to_dev(xs, "bf16")
+
+
+def _ref(p, xs):
+    return oracle.default().qmv_mxfp4(p.w_packed, p.scales, xs, x_dtype=oracle.BF16, nthreads=16)
+
+
+def _bits(t):
+    return t.contiguous().view(torch.int32 if t.dtype == torch.float32 else torch.int16)
+
+
+CASES = [  # N, K, Ms
+    (67, 2080, (1, 3, 13)),      # 65 chunks: one full wave step and a 1-chunk tail
+    (1, 32, (1, 2)),             # one block, one row
+    (130, 4096, (2, 13)),        # two full wave steps
+    (33, 544, (1, 5, 27)),       # 27 vectors: three tiles
+    (200, 32768, (1, 4)),        # long K: two vectors per launch
+    (5, 65536, (1, 3)),          # the longest K
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"N{c[0]}_K{c[1]}")
+def test_mx_small_vs_oracle(case):
+    N, K, Ms = case
+    p = gen.make_mx_problem(N, K, "bf16", seed=N + K)
+    w, s = _dev(p)
+    xs, xd = _x(p, max(Ms))
+    for M in Ms:
+        U.say(f"mxfp4 N={N} K={K} M={M}")
+        y = U.q.mxfp4(w, s, xd[:M], out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        U.check_parity(y, _ref(p, xs[:M]), f"mxfp4 N={N} K={K} M={M}")
+        y16 = U.q.mxfp4(w, s, xd[:M], out_dtype=torch.bfloat16)
+        torch.cuda.synchronize()
+        assert torch.equal(y16.view(torch.int16), U.rne_bf16(y).view(torch.int16))
+        for m in range(M):
+            one = U.q.mxfp4(w, s, xd[m:m + 1], out_dtype=torch.float32)
+            torch.cuda.synchronize()
+            assert torch.equal(_bits(y[m]), _bits(one[0])), f"M={M} vector {m}"
+
+
+def test_mx_workload_up_15360x3840():
+    p = gen.make_mx_problem(15360, 3840, "bf16", seed=4001)
+    w, s = _dev(p)
+    xs, xd = _x(p, 13)
+    for M in (1, 13):
+        U.say(f"mxfp4 15360x3840 M={M}")
+        y = U.q.mxfp4(w, s, xd[:M], out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        U.check_parity(y, _ref(p, xs[:M]), f"mxfp4 15360x3840 M={M}")
+
+
+def test_mx_readout_exact():
+    # scale 1 (E = 127) and x = e_k: y[m][n] is the E2M1 value of q[n][k_m] exactly
+    import json, os
+    table = np.array(json.load(open(os.path.join(os.path.dirname(__file__), "golden", "mxfp4_e2m1.json")))["e2m1"])
+    N, K = 37, 4096
+    p = gen.make_mx_problem(N, K, "bf16", seed=9, keep_q=True)
+    p.scales[:] = 127
+    w, s = _dev(p)
+    ks = [0, 1, 31, 32, 63, 64, 2047, 2048, 4000, 4095]
+    x = np.zeros((len(ks), K), dtype=np.float32)
+    x[np.arange(len(ks)), ks] = 1.0
+    xd = torch.from_numpy(x).to(torch.bfloat16).to(U.DEV)
+    U.say("mxfp4 read-out")
+    y = U.q.mxfp4(w, s, xd, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert np.array_equal(y.cpu().numpy(), table[p.q[:, ks].T].astype(np.float32))
