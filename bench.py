@@ -23,6 +23,9 @@ Prints one JSON line (the driver's contract) with extra objects:
                        the same byte count, with the same rotation: the share of
                        the peak any one-launch kernel of this size reaches
     m13             -- the same matrix at M = 13
+    mxfp4           -- the mxfp4 mode (E2M1 codes, E8M0 scale per 32 values) on
+                       the same shape at M = 1 and 13: us/call and GB/s of its
+                       algorithmic bytes N*K/2 + N*K/32 + M*K*2 + M*N*2
     occupancy_17408x5120 -- resources per rows-per-wavefront on the 27B-class
                        up-projection (no launch)
     cpu_baseline    -- the CPU oracle on the machine's host cores (bounded sample),
@@ -49,6 +52,12 @@ PEAK_GBS = 8000.0           # MI355X HBM3E
 PEAK_DOT_TFLOPS = 256 * 64 * 2.4e9 * 4 / 1e12
 ROTATE_BYTES = 1 << 30      # >= 4x the 256 MB Infinity Cache
 KERNEL_SOURCES = ("bit_quantized_gemv_amd/csrc/qmv_kernel.hpp",)
+
+
+def mx_bytes(N, K, M, y_bytes=2):
+    """Algorithmic bytes of one mxfp4 call: E2M1 codes, one E8M0 byte per 32
+    values, bf16 x, the output."""
+    return N * K // 2 + N * (K // 32) + M * K * 2 + M * N * y_bytes
 
 
 def alg_bytes(N, K, bits, gs, M, x_bytes=2, y_bytes=2, sb_bytes=2):
@@ -302,6 +311,29 @@ def main():
     gbs_stream = nb1 / (us_stream * 1e-6) / 1e9
     del SB
 
+    # mxfp4 mode on the same shape: M = 1 and 13, same rotation and graph timing
+    pm = gen.make_mx_problem(N, K, "bf16", seed=4001)
+    mw0 = torch.from_numpy(pm.w_packed.view(np.int32)).to(dev)
+    ms0 = torch.from_numpy(pm.scales).to(dev)
+    mx_copies = max(2, -(-ROTATE_BYTES // mx_bytes(N, K, Mmax)))
+    MW = [mw0.clone() for _ in range(mx_copies)]
+    MS = [ms0.clone() for _ in range(mx_copies)]
+
+    def launch_mx(i, M, stream):
+        st = q.mxfp4_ptr(MW[i].data_ptr(), MS[i].data_ptr(), X[i % ncopies].data_ptr(),
+                         Y[i % ncopies].data_ptr(), M, N, K, q.DT_BF16, stream.cuda_stream)
+        if st != 0:
+            raise q.QmvError(st, "qmv_mxfp4")
+
+    mx = {"workload": f"mxfp4_{N}x{K}", "format": "E2M1 codes, E8M0 scale per 32 values, bf16 x and y"}
+    for M in (1, Mmax):
+        us_mx, _ = time_calls(launch_mx, mx_copies, M, args.steps, args.warmup, torch)
+        nbm = mx_bytes(N, K, M)
+        mx[f"M{M}"] = {"us_per_call": round(us_mx, 3), "GB/s": round(nbm / (us_mx * 1e-6) / 1e9, 1),
+                       "pct_of_hbm_peak": round(100 * nbm / (us_mx * 1e-6) / 1e9 / PEAK_GBS, 2),
+                       "alg_bytes_per_launch": nbm}
+    del MW, MS
+
     occupancy = {}
     for M in (1, Mmax):
         for R in (1, 2, 3, 4):
@@ -356,6 +388,7 @@ def main():
             "qmv_frac_of_ceiling": round(r1["gbs"] / gbs_stream, 4),
         },
         "occupancy_17408x5120": occupancy,
+        "mxfp4": mx,
         "m13": {
             "M": Mmax,
             "us_per_call": round(r13["us"], 3),

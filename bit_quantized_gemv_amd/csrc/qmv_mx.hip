@@ -84,13 +84,30 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void qmv_mx_kernel(MxParams p)
     const int grid = gridDim.x;
     if ((int)blockIdx.x >= p.n_rb) return;
 
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(p.w, -1);
+    const __amdgpu_buffer_rsrc_t sr = make_rsrc(p.s, -1);
+    uint4 wb[2][R];
+    uint32_t eb[2][R];
+    // loads of step t of row block rb (rows past N read row N-1, chunks past
+    // the row's end its last chunk)
+    auto issue = [&](int slot, int rb, int t) {
+        const int n0 = (rb * W + wave) * R;
+        const int c = min(t * kWave + lane, p.chunks - 1);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int n = min(n0 + r, p.N - 1);
+            wb[slot][r] = buf_load_nt(wr, n * p.row_bytes + c * 16, 0);
+            eb[slot][r] = __builtin_amdgcn_raw_buffer_load_b8(sr, n * p.chunks + c, 0, 0);
+        }
+    };
+
     // ---- stage x: 16-byte pieces, four per chunk; pieces of chunks past the
     // row's end are zero.  All of a thread's loads are issued before any store.
     {
         const int cpad = p.nsteps * kWave;
         const int items = M * cpad * 4;
         const __amdgpu_buffer_rsrc_t xr = make_rsrc(p.x, M * p.K * 2);
-        for (int i0 = 0; i0 < items; i0 += 8 * (int)blockDim.x) {
+        auto batch = [&](int i0, auto first_tag) {
             uint4 v[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
@@ -99,6 +116,8 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void qmv_mx_kernel(MxParams p)
                 const int c = min(rem >> 2, p.chunks - 1), piece = rem & 3;
                 v[j] = buf_load(xr, (m * p.K + c * 32 + piece * 8) * 2);
             }
+            // the first weight step rides behind the first activation loads
+            if constexpr (decltype(first_tag)::value) issue(0, blockIdx.x, 0);
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int i = i0 + j * (int)blockDim.x + (int)threadIdx.x;
@@ -109,43 +128,31 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void qmv_mx_kernel(MxParams p)
                     *reinterpret_cast<uint4*>(lds + m * p.xm_bytes + lds_phys(c * 64 + piece * 16)) = d;
                 }
             }
-        }
+        };
+        batch(0, std::true_type{});
+        for (int i0 = 8 * (int)blockDim.x; i0 < items; i0 += 8 * (int)blockDim.x) batch(i0, std::false_type{});
     }
     __syncthreads();
 
-    const __amdgpu_buffer_rsrc_t wr = make_rsrc(p.w, -1);
-    const __amdgpu_buffer_rsrc_t sr = make_rsrc(p.s, -1);
     for (int rb = blockIdx.x; rb < p.n_rb; rb += grid) {
         const int n0 = (rb * W + wave) * R;
-        int roff[R], soff[R];
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const int n = min(n0 + r, p.N - 1);
-            roff[r] = n * p.row_bytes;
-            soff[r] = n * p.chunks;
-        }
         float acc[R][M];
 #pragma unroll
         for (int r = 0; r < R; ++r)
 #pragma unroll
             for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
 
-        uint4 wb[2][R];
-        uint32_t eb[2][R];
-        auto issue = [&](int slot, int t) {
-            const int c = min(t * kWave + lane, p.chunks - 1);
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-                wb[slot][r] = buf_load_nt(wr, roff[r] + c * 16, 0);
-                eb[slot][r] = __builtin_amdgcn_raw_buffer_load_b8(sr, soff[r] + c, 0, 0);
-            }
-        };
         // one step: the next step's loads go out, then this step's chunk is
         // decoded and every vector's chain and fold run (the slot is a
         // compile-time constant, so the ring stays in registers)
         auto step = [&](auto slot_tag, int t) {
             constexpr int slot = decltype(slot_tag)::value;
-            issue(slot ^ 1, min(t + 1, p.nsteps - 1));
+            // next loads: this row block's next step; after its last step, the
+            // next row block's first step when that lands in slot 0 (an even
+            // step count), else a harmless reload of this step
+            const bool last = t + 1 == p.nsteps;
+            const bool cross = last && rb + grid < p.n_rb && (p.nsteps & 1) == 0;
+            issue(slot ^ 1, cross ? rb + grid : rb, cross ? 0 : min(t + 1, p.nsteps - 1));
             __builtin_amdgcn_sched_barrier(0);
             const int c = t * kWave + lane;
             uint32_t pr[R][16];
@@ -185,7 +192,10 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void qmv_mx_kernel(MxParams p)
             }
             __builtin_amdgcn_sched_barrier(0);
         };
-        issue(0, 0);
+        // the first row block's first step went out with the activation loads,
+        // a later one's with the previous row block's last step (even step
+        // counts)
+        if (rb != (int)blockIdx.x && (p.nsteps & 1) != 0) issue(0, rb, 0);
         for (int t = 0; t < p.nsteps; t += 2) {
             step(std::integral_constant<int, 0>{}, t);
             if (t + 1 < p.nsteps) step(std::integral_constant<int, 1>{}, t + 1);
@@ -329,7 +339,12 @@ extern "C" int qmv_mxfp4(const uint32_t* w_packed, const uint8_t* scales, const 
         const int lds = Mt * p.xm_bytes;
         const int nb = mx_resident(fn, dev, lds);
         if (nb <= 0) return QMV_E_LAUNCH;
-        const int grid = std::min(p.n_rb, nb * cus);
+        // row blocks per workgroup: as the affine launch -- every workgroup the
+        // same count, and two for memory-bound calls while that still leaves a
+        // workgroup for every compute unit
+        int per = (p.n_rb + nb * cus - 1) / (nb * cus);
+        if (Mt <= 2 && per == 1 && p.n_rb >= 2 * cus) per = 2;
+        const int grid = (p.n_rb + per - 1) / per;
         // the kernel's row offsets are 32-bit
         if ((size_t)N * (size_t)p.row_bytes >= (size_t)1 << 31) return QMV_E_SHAPE;
         void* args[] = {&p};
