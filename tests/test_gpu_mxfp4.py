@@ -89,3 +89,34 @@ def test_mx_readout_exact():
     y = U.q.mxfp4(w, s, xd, out_dtype=torch.float32)
     torch.cuda.synchronize()
     assert np.array_equal(y.cpu().numpy(), table[p.q[:, ks].T].astype(np.float32))
+
+
+def _random_cases(n=60, seed=4242):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        K = 32 * int(rng.integers(1, 257))
+        N = int(rng.integers(1, 321))
+        M = int(rng.choice([1, 2, 3, 4, 5, 7, 9, 13, 14, 20, 27]))
+        out.append((N, K, M, 6000 + i))
+    return out
+
+
+@pytest.mark.parametrize("case", _random_cases(), ids=lambda c: f"N{c[0]}_K{c[1]}_M{c[2]}")
+def test_mx_random_shape_vs_oracle(case):
+    # seeded random shapes (ragged N, K from one block up, M up to 27) against
+    # the oracle, bf16 rounding and the one-vector calls of the first and last vector
+    N, K, M, seed = case
+    p = gen.make_mx_problem(N, K, "bf16", seed=seed)
+    w, s = _dev(p)
+    xs, xd = _x(p, max(M, 13))
+    U.say(f"mxfp4 random N={N} K={K} M={M}")
+    y = U.q.mxfp4(w, s, xd[:M], out_dtype=torch.float32)
+    y16 = U.q.mxfp4(w, s, xd[:M], out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    U.check_parity(y, _ref(p, xs[:M]), f"mxfp4 N={N} K={K} M={M}")
+    assert torch.equal(y16.view(torch.int16), U.rne_bf16(y).view(torch.int16))
+    for m in sorted({0, M - 1}):
+        one = U.q.mxfp4(w, s, xd[m:m + 1], out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(y[m]), _bits(one[0])), f"vector {m}"
