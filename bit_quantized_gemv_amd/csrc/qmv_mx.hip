@@ -49,7 +49,9 @@ struct MxParams {
     int row_bytes;   // K / 2
     int n_rb;        // row blocks of W*R rows
     int y_bf16;
-    int xm_bytes;    // LDS bytes of one vector (nsteps*64 chunks of 64 B, padded)
+    int win_steps;   // wave steps per K window (even unless one window covers K)
+    int nwin;        // K windows
+    int xm_bytes;    // LDS bytes of one vector's window (win_steps*64 chunks of 64 B, padded)
 };
 
 // 2^(E - 127) as fp32 from an E8M0 byte: E = 0 is the subnormal 2^-127 and
@@ -71,7 +73,11 @@ __device__ __forceinline__ uint4 fp4_word_to_bf16_pairs(uint32_t w)
                       __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 3)));
 }
 
-template <int R, int M>
+// WIN: the activations do not fit in LDS whole for this launch; they are
+// staged window by window (win_steps wave steps at a time) for every row block,
+// with the accumulators kept in registers across windows, which gives the
+// same bits as staging them whole.
+template <int R, int M, bool WIN>
 __global__ __launch_bounds__(kMaxWaves * kWave) void qmv_mx_kernel(MxParams p)
 {
     constexpr int V = R * M;
@@ -101,38 +107,43 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void qmv_mx_kernel(MxParams p)
         }
     };
 
-    // ---- stage x: 16-byte pieces, four per chunk; pieces of chunks past the
-    // row's end are zero.  All of a thread's loads are issued before any store.
-    {
-        const int cpad = p.nsteps * kWave;
-        const int items = M * cpad * 4;
-        const __amdgpu_buffer_rsrc_t xr = make_rsrc(p.x, M * p.K * 2);
-        auto batch = [&](int i0, auto first_tag) {
+    // ---- stage x[0..M)[window]: 16-byte pieces, four per chunk; pieces of
+    // chunks past the row's end are zero.  All of a thread's loads of a batch
+    // are issued before any store; the first batch of the first window carries
+    // the first weight step behind it.
+    const int cwin = p.win_steps * kWave;                 // chunks per window
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(p.x, M * p.K * 2);
+    auto stage = [&](int win, auto first_tag) {
+        const int items = M * cwin * 4;
+        const int c0 = win * cwin;
+        auto batch = [&](int i0, auto with_issue) {
             uint4 v[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int i = min(i0 + j * (int)blockDim.x + (int)threadIdx.x, items - 1);
-                const int m = i / (cpad * 4), rem = i - m * (cpad * 4);
-                const int c = min(rem >> 2, p.chunks - 1), piece = rem & 3;
+                const int m = i / (cwin * 4), rem = i - m * (cwin * 4);
+                const int c = min(c0 + (rem >> 2), p.chunks - 1), piece = rem & 3;
                 v[j] = buf_load(xr, (m * p.K + c * 32 + piece * 8) * 2);
             }
-            // the first weight step rides behind the first activation loads
-            if constexpr (decltype(first_tag)::value) issue(0, blockIdx.x, 0);
+            if constexpr (decltype(with_issue)::value) issue(0, blockIdx.x, 0);
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int i = i0 + j * (int)blockDim.x + (int)threadIdx.x;
                 if (i < items) {
-                    const int m = i / (cpad * 4), rem = i - m * (cpad * 4);
-                    const int c = rem >> 2, piece = rem & 3;
-                    const uint4 d = (c < p.chunks) ? v[j] : make_uint4(0, 0, 0, 0);
-                    *reinterpret_cast<uint4*>(lds + m * p.xm_bytes + lds_phys(c * 64 + piece * 16)) = d;
+                    const int m = i / (cwin * 4), rem = i - m * (cwin * 4);
+                    const int cl = rem >> 2, piece = rem & 3;
+                    const uint4 d = (c0 + cl < p.chunks) ? v[j] : make_uint4(0, 0, 0, 0);
+                    *reinterpret_cast<uint4*>(lds + m * p.xm_bytes + lds_phys(cl * 64 + piece * 16)) = d;
                 }
             }
         };
-        batch(0, std::true_type{});
+        batch(0, first_tag);
         for (int i0 = 8 * (int)blockDim.x; i0 < items; i0 += 8 * (int)blockDim.x) batch(i0, std::false_type{});
+    };
+    if constexpr (!WIN) {
+        stage(0, std::true_type{});
+        __syncthreads();
     }
-    __syncthreads();
 
     for (int rb = blockIdx.x; rb < p.n_rb; rb += grid) {
         const int n0 = (rb * W + wave) * R;
@@ -154,7 +165,7 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void qmv_mx_kernel(MxParams p)
             const bool cross = last && rb + grid < p.n_rb && (p.nsteps & 1) == 0;
             issue(slot ^ 1, cross ? rb + grid : rb, cross ? 0 : min(t + 1, p.nsteps - 1));
             __builtin_amdgcn_sched_barrier(0);
-            const int c = t * kWave + lane;
+            const int cl = (t - (t / p.win_steps) * p.win_steps) * kWave + lane;   // chunk in its window
             uint32_t pr[R][16];
             float sc[R];
 #pragma unroll
@@ -170,7 +181,7 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void qmv_mx_kernel(MxParams p)
                 }
                 sc[r] = e8m0_to_f32(eb[slot][r] & 0xffu);
             }
-            const uint8_t* xs = lds + lds_phys(c * 64);
+            const uint8_t* xs = lds + lds_phys(cl * 64);
 #pragma unroll
             for (int m = 0; m < M; ++m) {
                 uint32_t xp[16];
@@ -196,9 +207,23 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void qmv_mx_kernel(MxParams p)
         // a later one's with the previous row block's last step (even step
         // counts)
         if (rb != (int)blockIdx.x && (p.nsteps & 1) != 0) issue(0, rb, 0);
-        for (int t = 0; t < p.nsteps; t += 2) {
-            step(std::integral_constant<int, 0>{}, t);
-            if (t + 1 < p.nsteps) step(std::integral_constant<int, 1>{}, t + 1);
+        for (int win = 0; win < p.nwin; ++win) {
+            if constexpr (WIN) {
+                // every wavefront is past the previous window's reads
+                if (win > 0 || rb != (int)blockIdx.x) __syncthreads();
+                if (win == 0 && rb == (int)blockIdx.x)
+                    stage(win, std::true_type{});
+                else
+                    stage(win, std::false_type{});
+                __syncthreads();
+            }
+            // windows hold an even number of steps (all but the last), so every
+            // window starts on slot 0
+            const int t1 = min(p.nsteps, (win + 1) * p.win_steps);
+            for (int t = win * p.win_steps; t < t1; t += 2) {
+                step(std::integral_constant<int, 0>{}, t);
+                if (t + 1 < t1) step(std::integral_constant<int, 1>{}, t + 1);
+            }
         }
 
         // row totals: lane l ends with value reduce_index<P>(l)
@@ -227,18 +252,19 @@ namespace {
 
 using MxKernelFn = void (*)(qmv::MxParams);
 
-template <int R, int... Ms>
+template <int R, bool WIN, int... Ms>
 constexpr MxKernelFn mx_pick(int M, std::integer_sequence<int, Ms...>)
 {
     MxKernelFn f = nullptr;
-    ((f = (M == Ms + 1) ? &qmv::qmv_mx_kernel<R, Ms + 1> : f), ...);
+    ((f = (M == Ms + 1) ? &qmv::qmv_mx_kernel<R, Ms + 1, WIN> : f), ...);
     return f;
 }
 
-MxKernelFn mx_kernel(int R, int M)
+MxKernelFn mx_kernel(int R, int M, bool win)
 {
     const auto seq = std::make_integer_sequence<int, QMV_TILE_M>{};
-    return R == 2 ? mx_pick<2>(M, seq) : mx_pick<4>(M, seq);
+    if (win) return R == 2 ? mx_pick<2, true>(M, seq) : mx_pick<4, true>(M, seq);
+    return R == 2 ? mx_pick<2, false>(M, seq) : mx_pick<4, false>(M, seq);
 }
 
 constexpr int kMxW = 8;                      // wavefronts per workgroup
@@ -250,16 +276,44 @@ bool overlap_mx(const void* a, size_t na, const void* b, size_t nb)
     return pa < pb + nb && pb < pa + na;
 }
 
-int mx_xm_bytes(int K)
+constexpr int kMxStepBytes = qmv::kWave * 64 * 17 / 16;   // one vector's wave step in LDS (padded)
+
+int mx_steps(int K) { return (K / 32 + qmv::kWave - 1) / qmv::kWave; }
+
+// Rows per wavefront: four (activations read once per four rows) when M >= 3
+// and the row blocks still cover every compute unit, else two.  A K-windowed
+// launch also takes four when two would give workgroups more than one row
+// block (each would restage every window per row block).
+int mx_rows(int Mt, int N, int cus, bool win)
 {
-    const int nsteps = (K / 32 + qmv::kWave - 1) / qmv::kWave;
-    return nsteps * qmv::kWave * 64 * 17 / 16;   // 16 bytes of padding per 256
+    const int n_rb4 = (N + kMxW * 4 - 1) / (kMxW * 4);
+    const int n_rb2 = (N + kMxW * 2 - 1) / (kMxW * 2);
+    return (Mt >= 3 && (n_rb4 >= cus || (win && n_rb2 > cus))) ? 4 : 2;
 }
 
-// vectors per launch: at most QMV_TILE_M, and as many as fit in LDS whole
-int mx_vectors_per_launch(int K)
+// Vectors per launch and K windows.  Activations that fit in LDS whole for
+// all of a launch's vectors are staged once.  Otherwise the launch keeps up to
+// QMV_TILE_M vectors and stages K in windows of an even number of wave steps
+// (one pass over the weights), unless four-row blocks would still outnumber
+// the compute units -- each workgroup would then restage every window for
+// each of its row blocks -- and two tiles that fit whole suffice (two passes
+// over the weights, no restaging).
+struct MxShape {
+    int per_launch;   // vectors per launch (before balancing)
+    int win_steps;    // 0 = whole K
+};
+
+MxShape mx_shape(int M, int N, int K, int cus)
 {
-    return std::min(QMV_TILE_M, kMxLds / mx_xm_bytes(K));
+    const int nsteps = mx_steps(K);
+    const int whole = kMxLds / (nsteps * kMxStepBytes);
+    const int Mt = std::min(M, QMV_TILE_M);
+    if (whole >= Mt) return {QMV_TILE_M, 0};
+    const int n_rb4 = (N + kMxW * 4 - 1) / (kMxW * 4);
+    if (whole >= 1 && n_rb4 > cus && (Mt + whole - 1) / whole <= 2) return {whole, 0};
+    int ws = kMxLds / (Mt * kMxStepBytes);
+    ws -= ws & 1;
+    return {QMV_TILE_M, std::max(2, ws)};
 }
 
 std::mutex g_mx_mu;
@@ -313,16 +367,15 @@ extern "C" int qmv_mxfp4(const uint32_t* w_packed, const uint8_t* scales, const 
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
         return QMV_E_LAUNCH;
     const size_t yb = (y_dt == QMV_DT_F32) ? 4 : 2;
-    const int per_launch = mx_vectors_per_launch(K);
-    const int tiles = (M + per_launch - 1) / per_launch;
+    const MxShape shape = mx_shape(M, N, K, cus);
+    const int tiles = (M + shape.per_launch - 1) / shape.per_launch;
     hipStream_t s = static_cast<hipStream_t>(stream);
     int m0 = 0;
     for (int t = 0; t < tiles; ++t) {
         // balanced tiles: the first M % tiles get one more vector
         const int Mt = M / tiles + (t < M % tiles ? 1 : 0);
-        const int R = (Mt <= 2) ? 2 : 4;
-        const MxKernelFn fn = mx_kernel(R, Mt);
-        if (!fn) return QMV_E_LAUNCH;
+        const bool win = shape.win_steps > 0 && Mt * mx_steps(K) * kMxStepBytes > kMxLds;
+        const int R = mx_rows(Mt, N, cus, win);
         qmv::MxParams p;
         p.w = w_packed;
         p.s = scales;
@@ -331,12 +384,17 @@ extern "C" int qmv_mxfp4(const uint32_t* w_packed, const uint8_t* scales, const 
         p.N = N;
         p.K = K;
         p.chunks = K / 32;
-        p.nsteps = (p.chunks + qmv::kWave - 1) / qmv::kWave;
+        p.nsteps = mx_steps(K);
         p.row_bytes = K / 2;
         p.n_rb = (N + kMxW * R - 1) / (kMxW * R);
         p.y_bf16 = (y_dt == QMV_DT_BF16) ? 1 : 0;
-        p.xm_bytes = mx_xm_bytes(K);
+        p.win_steps = win ? shape.win_steps : p.nsteps;
+        p.nwin = (p.nsteps + p.win_steps - 1) / p.win_steps;
+        p.xm_bytes = p.win_steps * kMxStepBytes;
         const int lds = Mt * p.xm_bytes;
+        if (lds > kMxLds) return QMV_E_SHAPE;
+        const MxKernelFn fn = mx_kernel(R, Mt, win);
+        if (!fn) return QMV_E_LAUNCH;
         const int nb = mx_resident(fn, dev, lds);
         if (nb <= 0) return QMV_E_LAUNCH;
         // row blocks per workgroup: as the affine launch -- every workgroup the
