@@ -179,8 +179,10 @@ int qmv_stream_read(const void* buf, long long bytes, uint32_t* out, int checksu
  * pairs in K order, folded once as acc = fma(2^(E-127), D, acc) in ascending
  * block order per lane, then a fixed 64-lane butterfly; every output vector
  * equals the one-vector call on that vector bit for bit.  Ownership, streams
- * and errors as for qmv_affine; at most QMV_TILE_M vectors per launch, fewer
- * when K is long (x is staged in LDS whole), more run as balanced tiles.
+ * and errors as for qmv_affine.  At most QMV_TILE_M vectors per launch (more
+ * run as balanced tiles); x is staged in LDS whole or, when it does not fit,
+ * in K windows (or, for many rows, as two tiles of vectors that fit whole) --
+ * none of which changes a result bit.
  */
 #define QMV_MX_MAX_K 65536
 int qmv_mxfp4(const uint32_t* w_packed, const uint8_t* scales, const void* x, void* y,
