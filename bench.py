@@ -188,7 +188,7 @@ def _cpu_model():
 def workload_table(args, q, gen, torch, np, dev):
     """Every 12B/27B-class workload at M = 1, 2, 4, 8, 13: us per call (graph
     replay over rotating copies as in the bench line, median of three replays)
-    and the default launch."""
+    and the default launch; then the mxfp4 mode on the four projection shapes."""
     for name in ("up_4b_15360x3840", "down_4b_3840x15360", "up_2b_15360x3840",
                  "up_4b_17408x5120", "down_4b_5120x17408"):
         p = gen.make_problem(name)
@@ -218,6 +218,28 @@ def workload_table(args, q, gen, torch, np, dev):
                               "rows_per_wave": inf["rows_per_wave"], "wg_size": inf["wg_size"],
                               "grid": inf["grid"], "k_windows": inf["k_windows"]}), flush=True)
         del copies, base
+        torch.cuda.empty_cache()
+    # the mxfp4 mode on the same four projection shapes
+    for N, K in ((15360, 3840), (3840, 15360), (17408, 5120), (5120, 17408)):
+        pm = gen.make_mx_problem(N, K, "bf16", seed=4001)
+        nc = max(2, -(-ROTATE_BYTES // mx_bytes(N, K, 13)))
+        copies = [(torch.from_numpy(pm.w_packed.view(np.int32)).to(dev), torch.from_numpy(pm.scales).to(dev))
+                  for _ in range(nc)]
+        xm = torch.from_numpy(pm.x.view(np.int16)).view(torch.bfloat16).to(dev)
+        ym = torch.empty(13, N, dtype=torch.bfloat16, device=dev)
+
+        def launch_mx(i, M, stream):
+            st = q.mxfp4_ptr(copies[i][0].data_ptr(), copies[i][1].data_ptr(), xm.data_ptr(), ym.data_ptr(),
+                             M, N, K, q.DT_BF16, stream.cuda_stream)
+            if st != 0:
+                raise q.QmvError(st, "qmv_mxfp4")
+
+        for M in (1, 2, 4, 8, 13):
+            us, _ = time_calls(launch_mx, nc, M, args.steps, args.warmup, torch, replays=3)
+            nb = mx_bytes(N, K, M)
+            print(json.dumps({"workload": f"mxfp4_{N}x{K}", "M": M, "us_per_call": round(us, 3),
+                              "GB/s": round(nb / (us * 1e-6) / 1e9, 1)}), flush=True)
+        del copies
         torch.cuda.empty_cache()
 
 
