@@ -52,6 +52,7 @@ PEAK_GBS = 8000.0           # MI355X HBM3E
 PEAK_DOT_TFLOPS = 256 * 64 * 2.4e9 * 4 / 1e12
 ROTATE_BYTES = 1 << 30      # >= 4x the 256 MB Infinity Cache
 KERNEL_SOURCES = ("bit_quantized_gemv_amd/csrc/qmv_kernel.hpp",)
+MX_KERNEL_SOURCES = ("bit_quantized_gemv_amd/csrc/qmv_kernel.hpp", "bit_quantized_gemv_amd/csrc/qmv_mx.hip")
 
 
 def mx_bytes(N, K, M, y_bytes=2):
@@ -64,12 +65,12 @@ def alg_bytes(N, K, bits, gs, M, x_bytes=2, y_bytes=2, sb_bytes=2):
     return N * K * bits // 8 + 2 * N * (K // gs) * sb_bytes + M * K * x_bytes + M * N * y_bytes
 
 
-def kernel_hash() -> str:
+def kernel_hash(sources=KERNEL_SOURCES) -> str:
     """Hash of the kernel source's code: comments and whitespace are dropped,
     so the counters stay attached to the code they were taken on."""
     import re
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in sources:
         with open(os.path.join(ROOT, f), encoding="utf-8") as fh:
             src = fh.read()
         src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
@@ -78,16 +79,16 @@ def kernel_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_for(M: int):
+def traffic_for(M: int, name="qmv_up_4b_15360x3840_traffic.json", sources=KERNEL_SOURCES):
     """HBM bytes per launch from the committed counter summary, if it was taken
     on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", "qmv_up_4b_15360x3840_traffic.json")
+    path = os.path.join(ROOT, "profiles", name)
     try:
         with open(path) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_hash") != kernel_hash():
+    if t.get("kernel_hash") != kernel_hash(sources):
         return None
     e = t.get("per_launch", {}).get(f"M{M}")
     return None if e is None else e.get("hbm_bytes")
@@ -351,9 +352,14 @@ def main():
     for M in (1, Mmax):
         us_mx, _ = time_calls(launch_mx, mx_copies, M, args.steps, args.warmup, torch)
         nbm = mx_bytes(N, K, M)
-        mx[f"M{M}"] = {"us_per_call": round(us_mx, 3), "GB/s": round(nbm / (us_mx * 1e-6) / 1e9, 1),
-                       "pct_of_hbm_peak": round(100 * nbm / (us_mx * 1e-6) / 1e9 / PEAK_GBS, 2),
-                       "alg_bytes_per_launch": nbm}
+        gbm = nbm / (us_mx * 1e-6) / 1e9
+        mx[f"M{M}"] = {"us_per_call": round(us_mx, 3), "GB/s": round(gbm, 1),
+                       "pct_of_hbm_peak": round(100 * gbm / PEAK_GBS, 2),
+                       "alg_bytes_per_launch": nbm,
+                       "roofline": {"bound": "hbm", "achieved": round(gbm, 1), "peak": PEAK_GBS,
+                                    "unit": "GB/s", "frac": round(gbm / PEAK_GBS, 4),
+                                    "traffic": traffic_for(M, "qmv_mx_15360x3840_traffic.json",
+                                                           MX_KERNEL_SOURCES)}}
     del MW, MS
 
     occupancy = {}
