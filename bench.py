@@ -231,7 +231,7 @@ def workload_table(args, q, gen, torch, np, dev):
 
         def launch_mx(i, M, stream):
             st = q.mxfp4_ptr(copies[i][0].data_ptr(), copies[i][1].data_ptr(), xm.data_ptr(), ym.data_ptr(),
-                             M, N, K, q.DT_BF16, stream.cuda_stream)
+                             M, N, K, q.DT_BF16, q.DT_BF16, stream.cuda_stream)
             if st != 0:
                 raise q.QmvError(st, "qmv_mxfp4")
 
@@ -344,7 +344,7 @@ def main():
 
     def launch_mx(i, M, stream):
         st = q.mxfp4_ptr(MW[i].data_ptr(), MS[i].data_ptr(), X[i % ncopies].data_ptr(),
-                         Y[i % ncopies].data_ptr(), M, N, K, q.DT_BF16, stream.cuda_stream)
+                         Y[i % ncopies].data_ptr(), M, N, K, q.DT_BF16, q.DT_BF16, stream.cuda_stream)
         if st != 0:
             raise q.QmvError(st, "qmv_mxfp4")
 

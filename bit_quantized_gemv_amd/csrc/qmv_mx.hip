@@ -3,8 +3,8 @@
 //   y[m][n] = sum_b X[n][b] * sum_{k in b} e2m1(q[n][k]) * x[m][k]
 //
 // with FP4 E2M1 codes q packed 8 per uint32 (field 0 in the low bits), one
-// E8M0 scale X = 2^(E - 127) per block of 32 values along K, and bf16
-// activations.  The MLX pages list this quantization mode beside the affine
+// E8M0 scale X = 2^(E - 127) per block of 32 values along K, and bf16 or
+// fp32 activations.  The MLX pages list this quantization mode beside the affine
 // one (mlxcel issue "an order-preserving streamed qmv would give MTP the fast
 // kernel and byte-identity together", section "Scope limits") without
 // defining the format; the element and scale formats are those of the OCP
@@ -14,8 +14,8 @@
 // one block per lane):
 //   * Chunk c (16 bytes = 32 codes = one block) of a row is read by lane c % 64
 //     in wave step c / 64; a wavefront owns R consecutive rows; a workgroup of
-//     W wavefronts stages x[0..M)[0..K) in LDS (bf16, natural order, zero past
-//     the row's last chunk) and walks row blocks of W*R rows.
+//     W wavefronts stages x[0..M)[0..K) in LDS (its own dtype, natural order,
+//     zero past the row's last chunk) and walks row blocks of W*R rows.
 //   * Per row, chunk and vector: the codes of each byte become an exact bf16
 //     pair (v_cvt_scalef32_pk_bf16_fp4 with scale 1: low nibble first); D is
 //     the v_dot2_f32_bf16 chain over the chunk's 16 pairs, in byte order,
@@ -40,7 +40,7 @@ namespace qmv {
 struct MxParams {
     const uint32_t* w;
     const uint8_t* s;
-    const uint16_t* x;
+    const void* x;
     void* y;
     int N;
     int K;
@@ -73,11 +73,26 @@ __device__ __forceinline__ uint4 fp4_word_to_bf16_pairs(uint32_t w)
                       __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 3)));
 }
 
+// The eight codes of a word as exact fp32 values, code 0 (low nibble of byte 0)
+// first.
+__device__ __forceinline__ void fp4_word_to_f32(uint32_t w, float (&out)[8])
+{
+    const auto p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+    const auto p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+    const auto p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+    const auto p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+    out[0] = p0[0]; out[1] = p0[1]; out[2] = p1[0]; out[3] = p1[1];
+    out[4] = p2[0]; out[5] = p2[1]; out[6] = p3[0]; out[7] = p3[1];
+}
+
 // WIN: the activations do not fit in LDS whole for this launch; they are
 // staged window by window (win_steps wave steps at a time) for every row block,
 // with the accumulators kept in registers across windows, which gives the
 // same bits as staging them whole.
-template <int R, int M, bool WIN>
+// XF32: fp32 activations -- each code becomes an exact fp32
+// (v_cvt_scalef32_pk_f32_fp4, scale 1) and the chunk's dot is the fma chain
+// over its 32 values in ascending k, from 0.
+template <int R, int M, bool WIN, bool XF32>
 __global__ __launch_bounds__(kMaxWaves * kWave) void qmv_mx_kernel(MxParams p)
 {
     constexpr int V = R * M;
@@ -112,28 +127,31 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void qmv_mx_kernel(MxParams p)
     // are issued before any store; the first batch of the first window carries
     // the first weight step behind it.
     const int cwin = p.win_steps * kWave;                 // chunks per window
-    const __amdgpu_buffer_rsrc_t xr = make_rsrc(p.x, M * p.K * 2);
+    constexpr int XB = XF32 ? 4 : 2;                      // activation bytes
+    constexpr int PPC = 32 * XB / 16;                     // 16-byte pieces per chunk
+    constexpr int CB = 32 * XB;                           // LDS bytes per chunk
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(p.x, M * p.K * XB);
     auto stage = [&](int win, auto first_tag) {
-        const int items = M * cwin * 4;
+        const int items = M * cwin * PPC;
         const int c0 = win * cwin;
         auto batch = [&](int i0, auto with_issue) {
             uint4 v[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int i = min(i0 + j * (int)blockDim.x + (int)threadIdx.x, items - 1);
-                const int m = i / (cwin * 4), rem = i - m * (cwin * 4);
-                const int c = min(c0 + (rem >> 2), p.chunks - 1), piece = rem & 3;
-                v[j] = buf_load(xr, (m * p.K + c * 32 + piece * 8) * 2);
+                const int m = i / (cwin * PPC), rem = i - m * (cwin * PPC);
+                const int c = min(c0 + rem / PPC, p.chunks - 1), piece = rem % PPC;
+                v[j] = buf_load(xr, (m * p.K + c * 32) * XB + piece * 16);
             }
             if constexpr (decltype(with_issue)::value) issue(0, blockIdx.x, 0);
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int i = i0 + j * (int)blockDim.x + (int)threadIdx.x;
                 if (i < items) {
-                    const int m = i / (cwin * 4), rem = i - m * (cwin * 4);
-                    const int cl = rem >> 2, piece = rem & 3;
+                    const int m = i / (cwin * PPC), rem = i - m * (cwin * PPC);
+                    const int cl = rem / PPC, piece = rem % PPC;
                     const uint4 d = (c0 + cl < p.chunks) ? v[j] : make_uint4(0, 0, 0, 0);
-                    *reinterpret_cast<uint4*>(lds + m * p.xm_bytes + lds_phys(cl * 64 + piece * 16)) = d;
+                    *reinterpret_cast<uint4*>(lds + m * p.xm_bytes + lds_phys(cl * CB + piece * 16)) = d;
                 }
             }
         };
@@ -166,40 +184,75 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void qmv_mx_kernel(MxParams p)
             issue(slot ^ 1, cross ? rb + grid : rb, cross ? 0 : min(t + 1, p.nsteps - 1));
             __builtin_amdgcn_sched_barrier(0);
             const int cl = (t - (t / p.win_steps) * p.win_steps) * kWave + lane;   // chunk in its window
-            uint32_t pr[R][16];
             float sc[R];
 #pragma unroll
-            for (int r = 0; r < R; ++r) {
-                const uint32_t wd[4] = {wb[slot][r].x, wb[slot][r].y, wb[slot][r].z, wb[slot][r].w};
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const uint4 q4 = fp4_word_to_bf16_pairs(wd[i]);
-                    pr[r][4 * i] = q4.x;
-                    pr[r][4 * i + 1] = q4.y;
-                    pr[r][4 * i + 2] = q4.z;
-                    pr[r][4 * i + 3] = q4.w;
-                }
-                sc[r] = e8m0_to_f32(eb[slot][r] & 0xffu);
-            }
-            const uint8_t* xs = lds + lds_phys(cl * 64);
-#pragma unroll
-            for (int m = 0; m < M; ++m) {
-                uint32_t xp[16];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const uint4 q = *reinterpret_cast<const uint4*>(xs + m * p.xm_bytes + 16 * i);
-                    xp[4 * i] = q.x;
-                    xp[4 * i + 1] = q.y;
-                    xp[4 * i + 2] = q.z;
-                    xp[4 * i + 3] = q.w;
-                }
+            for (int r = 0; r < R; ++r) sc[r] = e8m0_to_f32(eb[slot][r] & 0xffu);
+            const uint8_t* xs = lds + lds_phys(cl * CB);
+            if constexpr (!XF32) {
+                uint32_t pr[R][16];
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
-                    float d = 0.0f;
+                    const uint32_t wd[4] = {wb[slot][r].x, wb[slot][r].y, wb[slot][r].z, wb[slot][r].w};
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) d = dot2(pr[r][i], xp[i], d);
-                    acc[r][m] = pinned(__builtin_fmaf(sc[r], d, acc[r][m]));
+                    for (int i = 0; i < 4; ++i) {
+                        const uint4 q4 = fp4_word_to_bf16_pairs(wd[i]);
+                        pr[r][4 * i] = q4.x;
+                        pr[r][4 * i + 1] = q4.y;
+                        pr[r][4 * i + 2] = q4.z;
+                        pr[r][4 * i + 3] = q4.w;
+                    }
                 }
+#pragma unroll
+                for (int m = 0; m < M; ++m) {
+                    uint32_t xp[16];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const uint4 q = *reinterpret_cast<const uint4*>(xs + m * p.xm_bytes + 16 * i);
+                        xp[4 * i] = q.x;
+                        xp[4 * i + 1] = q.y;
+                        xp[4 * i + 2] = q.z;
+                        xp[4 * i + 3] = q.w;
+                    }
+#pragma unroll
+                    for (int r = 0; r < R; ++r) {
+                        float d = 0.0f;
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) d = dot2(pr[r][i], xp[i], d);
+                        acc[r][m] = pinned(__builtin_fmaf(sc[r], d, acc[r][m]));
+                    }
+                }
+            } else {
+                // one word (8 values) of every row at a time; each (row, vector)
+                // chain runs through the words in order
+                float d[R][M];
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+#pragma unroll
+                    for (int m = 0; m < M; ++m) d[r][m] = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float cv[R][8];
+#pragma unroll
+                    for (int r = 0; r < R; ++r) {
+                        const uint32_t w = (i == 0) ? wb[slot][r].x : (i == 1) ? wb[slot][r].y
+                                         : (i == 2) ? wb[slot][r].z : wb[slot][r].w;
+                        fp4_word_to_f32(w, cv[r]);
+                    }
+#pragma unroll
+                    for (int m = 0; m < M; ++m) {
+                        const float4 xa = *reinterpret_cast<const float4*>(xs + m * p.xm_bytes + 32 * i);
+                        const float4 xb = *reinterpret_cast<const float4*>(xs + m * p.xm_bytes + 32 * i + 16);
+                        const float xv[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+#pragma unroll
+                        for (int r = 0; r < R; ++r)
+#pragma unroll
+                            for (int k = 0; k < 8; ++k) d[r][m] = __builtin_fmaf(cv[r][k], xv[k], d[r][m]);
+                    }
+                }
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+#pragma unroll
+                    for (int m = 0; m < M; ++m) acc[r][m] = pinned(__builtin_fmaf(sc[r], d[r][m], acc[r][m]));
             }
             __builtin_amdgcn_sched_barrier(0);
         };
@@ -252,19 +305,28 @@ namespace {
 
 using MxKernelFn = void (*)(qmv::MxParams);
 
-template <int R, bool WIN, int... Ms>
+template <int R, bool WIN, bool XF32, int... Ms>
 constexpr MxKernelFn mx_pick(int M, std::integer_sequence<int, Ms...>)
 {
     MxKernelFn f = nullptr;
-    ((f = (M == Ms + 1) ? &qmv::qmv_mx_kernel<R, Ms + 1, WIN> : f), ...);
+    ((f = (M == Ms + 1) ? &qmv::qmv_mx_kernel<R, Ms + 1, WIN, XF32> : f), ...);
     return f;
 }
 
-MxKernelFn mx_kernel(int R, int M, bool win)
+// fp32 activations: two rows per wavefront and at most kMxF32Tile vectors per
+// launch (their chains and accumulators stay in registers).
+constexpr int kMxF32Tile = 4;
+
+MxKernelFn mx_kernel(int R, int M, bool win, bool xf32)
 {
+    if (xf32) {
+        const auto seq = std::make_integer_sequence<int, kMxF32Tile>{};
+        if (R != 2 || M > kMxF32Tile) return nullptr;
+        return win ? mx_pick<2, true, true>(M, seq) : mx_pick<2, false, true>(M, seq);
+    }
     const auto seq = std::make_integer_sequence<int, QMV_TILE_M>{};
-    if (win) return R == 2 ? mx_pick<2, true>(M, seq) : mx_pick<4, true>(M, seq);
-    return R == 2 ? mx_pick<2, false>(M, seq) : mx_pick<4, false>(M, seq);
+    if (win) return R == 2 ? mx_pick<2, true, false>(M, seq) : mx_pick<4, true, false>(M, seq);
+    return R == 2 ? mx_pick<2, false, false>(M, seq) : mx_pick<4, false, false>(M, seq);
 }
 
 constexpr int kMxW = 8;                      // wavefronts per workgroup
@@ -276,7 +338,8 @@ bool overlap_mx(const void* a, size_t na, const void* b, size_t nb)
     return pa < pb + nb && pb < pa + na;
 }
 
-constexpr int kMxStepBytes = qmv::kWave * 64 * 17 / 16;   // one vector's wave step in LDS (padded)
+// one vector's wave step in LDS (padded): 64 chunks of 32 activations
+int mx_step_bytes(bool xf32) { return qmv::kWave * 32 * (xf32 ? 4 : 2) * 17 / 16; }
 
 int mx_steps(int K) { return (K / 32 + qmv::kWave - 1) / qmv::kWave; }
 
@@ -303,17 +366,18 @@ struct MxShape {
     int win_steps;    // 0 = whole K
 };
 
-MxShape mx_shape(int M, int N, int K, int cus)
+MxShape mx_shape(int M, int N, int K, int cus, bool xf32)
 {
+    const int tile = xf32 ? kMxF32Tile : QMV_TILE_M;
     const int nsteps = mx_steps(K);
-    const int whole = kMxLds / (nsteps * kMxStepBytes);
-    const int Mt = std::min(M, QMV_TILE_M);
-    if (whole >= Mt) return {QMV_TILE_M, 0};
+    const int whole = kMxLds / (nsteps * mx_step_bytes(xf32));
+    const int Mt = std::min(M, tile);
+    if (whole >= Mt) return {tile, 0};
     const int n_rb4 = (N + kMxW * 4 - 1) / (kMxW * 4);
     if (whole >= 1 && n_rb4 > cus && (Mt + whole - 1) / whole <= 2) return {whole, 0};
-    int ws = kMxLds / (Mt * kMxStepBytes);
+    int ws = kMxLds / (Mt * mx_step_bytes(xf32));
     ws -= ws & 1;
-    return {QMV_TILE_M, std::max(2, ws)};
+    return {tile, std::max(2, ws)};
 }
 
 std::mutex g_mx_mu;
@@ -338,18 +402,19 @@ int mx_resident(MxKernelFn fn, int dev, int lds)
 }
 
 int mx_check(const uint32_t* w, const uint8_t* s, const void* x, void* y, int M, int N, int K,
-             int y_dt)
+             int x_dt, int y_dt)
 {
     if (!w || !s || !x || !y) return QMV_E_NULL;
     if (M < 1 || M > QMV_MAX_M) return QMV_E_M_RANGE;
     if (N < 1 || N > QMV_MAX_N || K < 32 || K % 32 != 0 || K > QMV_MX_MAX_K) return QMV_E_SHAPE;
-    if (y_dt != QMV_DT_F32 && y_dt != QMV_DT_BF16) return QMV_E_DTYPE;
+    if ((x_dt != QMV_DT_F32 && x_dt != QMV_DT_BF16) || (y_dt != QMV_DT_F32 && y_dt != QMV_DT_BF16))
+        return QMV_E_DTYPE;
     const size_t yb = (y_dt == QMV_DT_F32) ? 4 : 2;
     if ((reinterpret_cast<uintptr_t>(w) % 16) || (reinterpret_cast<uintptr_t>(x) % 16) ||
         (reinterpret_cast<uintptr_t>(y) % yb))
         return QMV_E_ALIGN;
     const size_t nw = (size_t)N * (size_t)K / 2, ns = (size_t)N * (size_t)(K / 32);
-    const size_t nx = (size_t)M * (size_t)K * 2, ny = (size_t)M * (size_t)N * yb;
+    const size_t nx = (size_t)M * (size_t)K * (x_dt == QMV_DT_F32 ? 4 : 2), ny = (size_t)M * (size_t)N * yb;
     if (overlap_mx(y, ny, w, nw) || overlap_mx(y, ny, s, ns) || overlap_mx(y, ny, x, nx))
         return QMV_E_ALIAS;
     return QMV_OK;
@@ -358,28 +423,31 @@ int mx_check(const uint32_t* w, const uint8_t* s, const void* x, void* y, int M,
 }  // namespace
 
 extern "C" int qmv_mxfp4(const uint32_t* w_packed, const uint8_t* scales, const void* x, void* y,
-                         int M, int N, int K, qmv_dtype y_dt, void* stream)
+                         int M, int N, int K, qmv_dtype x_dt, qmv_dtype y_dt, void* stream)
 {
-    const int st = mx_check(w_packed, scales, x, y, M, N, K, (int)y_dt);
+    const int st = mx_check(w_packed, scales, x, y, M, N, K, (int)x_dt, (int)y_dt);
     if (st != QMV_OK) return st;
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess) return QMV_E_LAUNCH;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
         return QMV_E_LAUNCH;
     const size_t yb = (y_dt == QMV_DT_F32) ? 4 : 2;
-    const MxShape shape = mx_shape(M, N, K, cus);
+    const bool xf32 = x_dt == QMV_DT_F32;
+    const size_t xb = xf32 ? 4 : 2;
+    const int step_bytes = mx_step_bytes(xf32);
+    const MxShape shape = mx_shape(M, N, K, cus, xf32);
     const int tiles = (M + shape.per_launch - 1) / shape.per_launch;
     hipStream_t s = static_cast<hipStream_t>(stream);
     int m0 = 0;
     for (int t = 0; t < tiles; ++t) {
         // balanced tiles: the first M % tiles get one more vector
         const int Mt = M / tiles + (t < M % tiles ? 1 : 0);
-        const bool win = shape.win_steps > 0 && Mt * mx_steps(K) * kMxStepBytes > kMxLds;
-        const int R = mx_rows(Mt, N, cus, win);
+        const bool win = shape.win_steps > 0 && Mt * mx_steps(K) * step_bytes > kMxLds;
+        const int R = xf32 ? 2 : mx_rows(Mt, N, cus, win);
         qmv::MxParams p;
         p.w = w_packed;
         p.s = scales;
-        p.x = static_cast<const uint16_t*>(x) + (size_t)m0 * K;
+        p.x = static_cast<const uint8_t*>(x) + (size_t)m0 * K * xb;
         p.y = static_cast<uint8_t*>(y) + (size_t)m0 * N * yb;
         p.N = N;
         p.K = K;
@@ -390,10 +458,10 @@ extern "C" int qmv_mxfp4(const uint32_t* w_packed, const uint8_t* scales, const 
         p.y_bf16 = (y_dt == QMV_DT_BF16) ? 1 : 0;
         p.win_steps = win ? shape.win_steps : p.nsteps;
         p.nwin = (p.nsteps + p.win_steps - 1) / p.win_steps;
-        p.xm_bytes = p.win_steps * kMxStepBytes;
+        p.xm_bytes = p.win_steps * step_bytes;
         const int lds = Mt * p.xm_bytes;
         if (lds > kMxLds) return QMV_E_SHAPE;
-        const MxKernelFn fn = mx_kernel(R, Mt, win);
+        const MxKernelFn fn = mx_kernel(R, Mt, win, xf32);
         if (!fn) return QMV_E_LAUNCH;
         const int nb = mx_resident(fn, dev, lds);
         if (nb <= 0) return QMV_E_LAUNCH;

@@ -53,7 +53,7 @@ def lib():
         L.qmv_status_string.restype = ctypes.c_char_p
         L.qmv_stream_read.argtypes = [P, ctypes.c_longlong, P, I, P]
         L.qmv_stream_read.restype = I
-        L.qmv_mxfp4.argtypes = [P, P, P, P, I, I, I, I, P]
+        L.qmv_mxfp4.argtypes = [P, P, P, P, I, I, I, I, I, P]
         L.qmv_mxfp4.restype = I
         _lib = L
     return _lib
@@ -77,17 +77,17 @@ def stream_read_ptr(buf, nbytes, out, checksum=False, stream=0) -> int:
     return lib().qmv_stream_read(buf, nbytes, out, 1 if checksum else 0, stream)
 
 
-def mxfp4_ptr(w, s, x, y, M, N, K, y_dt=DT_BF16, stream=0) -> int:
+def mxfp4_ptr(w, s, x, y, M, N, K, x_dt=DT_BF16, y_dt=DT_BF16, stream=0) -> int:
     """Raw C-ABI call of the mxfp4 mode with integer device pointers; returns
     the status code."""
-    return lib().qmv_mxfp4(w, s, x, y, M, N, K, y_dt, stream)
+    return lib().qmv_mxfp4(w, s, x, y, M, N, K, x_dt, y_dt, stream)
 
 
 def mxfp4(w, scales, x, *, out=None, out_dtype=None, stream=None):
     """y[M][N] of the mxfp4 mode on the current (or given) torch stream.
 
     w: int32/uint32 [N][K/8] packed E2M1 codes (field 0 in the low bits);
-    scales: uint8 [N][K/32] E8M0 block scales; x: bf16 [M][K] (or [K]); out:
+    scales: uint8 [N][K/32] E8M0 block scales; x: bf16 or fp32 [M][K] (or [K]); out:
     optional fp32/bf16 [M][N] tensor, else allocated with out_dtype (default
     bf16).
     """
@@ -104,8 +104,8 @@ def mxfp4(w, scales, x, *, out=None, out_dtype=None, stream=None):
         raise TypeError("w must be int32 or uint32 packed words")
     if scales.dtype != torch.uint8:
         raise TypeError("scales must be uint8 (E8M0)")
-    if x.dtype != torch.bfloat16:
-        raise TypeError("x must be bf16")
+    if x.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("x must be bf16 or fp32")
     M, K = x.shape
     N = w.shape[0]
     if out is None:
@@ -114,7 +114,7 @@ def mxfp4(w, scales, x, *, out=None, out_dtype=None, stream=None):
         raise ValueError("out must be a contiguous [M][N] tensor")
     st = torch.cuda.current_stream(x.device) if stream is None else stream
     status = mxfp4_ptr(w.data_ptr(), scales.data_ptr(), x.data_ptr(), out.data_ptr(), M, N, K,
-                       _dt_of(out, "out"), st.cuda_stream)
+                       _dt_of(x, "x"), _dt_of(out, "out"), st.cuda_stream)
     if status != 0:
         raise QmvError(status, "qmv_mxfp4")
     return out[0] if squeeze else out

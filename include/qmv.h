@@ -171,22 +171,24 @@ int qmv_stream_read(const void* buf, long long bytes, uint32_t* out, int checksu
  *   w_packed  uint32 [N][K/8], code k of a row in field k % 8 (bits
  *             [4*(k%8), 4*(k%8)+4)) of word k / 8 -- field 0 in the low bits.
  *   scales    uint8 [N][K/32] (E8M0), no alignment requirement.
- *   x         bf16 [M][K]; y [M][N] of y_dt (QMV_DT_F32 or QMV_DT_BF16, RNE).
+ *   x         [M][K] of x_dt (QMV_DT_BF16 or QMV_DT_F32); y [M][N] of y_dt
+ *             (QMV_DT_F32 or QMV_DT_BF16, RNE).
  *   M in [1, QMV_MAX_M]; N in [1, QMV_MAX_N]; K a multiple of 32 in
  *   [32, QMV_MX_MAX_K] with N*K/2 < 2^31; w_packed and x 16-byte aligned, y
  *   aligned to its element size; y must not overlap an input.
  * Numerics: each block's dot is an fp32 v_dot2 chain over its exact bf16 code
- * pairs in K order, folded once as acc = fma(2^(E-127), D, acc) in ascending
- * block order per lane, then a fixed 64-lane butterfly; every output vector
+ * pairs in K order (fp32 x: an fma chain over its exact fp32 codes in K order),
+ * from 0, folded once as acc = fma(2^(E-127), D, acc) in ascending block order
+ * per lane, then a fixed 64-lane butterfly; every output vector
  * equals the one-vector call on that vector bit for bit.  Ownership, streams
- * and errors as for qmv_affine.  At most QMV_TILE_M vectors per launch (more
- * run as balanced tiles); x is staged in LDS whole or, when it does not fit,
+ * and errors as for qmv_affine.  At most QMV_TILE_M vectors per launch (fp32 x:
+ * four; more run as balanced tiles); x is staged in LDS whole or, when it does not fit,
  * in K windows (or, for many rows, as two tiles of vectors that fit whole) --
  * none of which changes a result bit.
  */
 #define QMV_MX_MAX_K 65536
 int qmv_mxfp4(const uint32_t* w_packed, const uint8_t* scales, const void* x, void* y,
-              int M, int N, int K, qmv_dtype y_dt, void* stream);
+              int M, int N, int K, qmv_dtype x_dt, qmv_dtype y_dt, void* stream);
 
 /* Static string naming a status code ("QMV_OK", "QMV_E_BITS", ...). */
 const char* qmv_status_string(int status);

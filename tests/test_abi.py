@@ -109,17 +109,22 @@ def test_stream_read_validates(L):
 
 
 def test_mxfp4_validates(L):
-    # argument errors of the mxfp4 mode return before any HIP call
+    # argument errors of the mxfp4 mode return before any HIP call; every call
+    # here fails validation, so none reaches a launch
     P, I = ctypes.c_void_p, ctypes.c_int
-    L.qmv_mxfp4.argtypes = [P, P, P, P, I, I, I, I, P]
+    L.qmv_mxfp4.argtypes = [P, P, P, P, I, I, I, I, I, P]
     w, s, x, y = 1 << 20, 1 << 24, 1 << 28, 1 << 32
     F32, F16, BF16 = 0, 1, 2
     call = lambda **k: L.qmv_mxfp4(k.get("w", w), k.get("s", s), k.get("x", x), k.get("y", y),
-                                   k.get("M", 1), k.get("N", 8), k.get("K", 64), k.get("dt", BF16), None)
+                                   k.get("M", 1), k.get("N", 8), k.get("K", 64), k.get("xdt", BF16),
+                                   k.get("dt", BF16), None)
     assert call(w=None) == 1 and call(s=None) == 1 and call(x=None) == 1 and call(y=None) == 1
     assert call(M=0) == 5 and call(M=65537) == 5                        # QMV_E_M_RANGE
     assert call(K=48) == 4 and call(K=16) == 4 and call(K=65536 + 32) == 4 and call(N=0) == 4
-    assert call(dt=F16) == 7                                            # QMV_E_DTYPE
+    assert call(dt=F16) == 7 and call(xdt=F16) == 7 and call(xdt=5) == 7  # QMV_E_DTYPE
     assert call(w=w + 8) == 6 and call(x=x + 8) == 6 and call(y=y + 2, dt=F32) == 6
     assert call(y=w + 64) == 9                                          # QMV_E_ALIAS
-    assert call(s=s + 1) != 6                                           # scales need no alignment
+    # one fp32 vector of K = 64 spans 256 bytes (bf16: 128)
+    assert call(y=x + 192, M=1, K=64, xdt=F32) == 9
+    # scales need no alignment: the call gets past the alignment checks to the alias check
+    assert call(s=s + 1, y=w + 64) == 9

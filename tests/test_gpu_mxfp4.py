@@ -1,7 +1,8 @@
 """GPU parity of the mxfp4 mode through the C ABI against the oracle: small
 shapes over wave-step tails and ragged row blocks, the longest K, tiles of
-vectors, the up-projection workload, exact read-out, bf16 rounding, and every
-output vector against the one-vector call bit for bit."""
+vectors, the up-projection workload, exact read-out, bf16 rounding, fp32
+activations, and every output vector against the one-vector call bit for
+bit."""
 import numpy as np
 import pytest
 import torch
@@ -19,13 +20,13 @@ def _dev(p):
     return w, s
 
 
-def _x(p, rows):
-    xs = gen.make_x(p.K, "bf16", 7 + p.N, rows=rows)
-    return xs, U.x_to_dev(xs, "bf16")
+def _x(p, rows, x_dtype="bf16"):
+    xs = gen.make_x(p.K, x_dtype, 7 + p.N, rows=rows)
+    return xs, U.x_to_dev(xs, x_dtype)
 
 
-def _ref(p, xs):
-    return oracle.default().qmv_mxfp4(p.w_packed, p.scales, xs, x_dtype=oracle.BF16, nthreads=16)
+def _ref(p, xs, x_dtype="bf16"):
+    return oracle.default().qmv_mxfp4(p.w_packed, p.scales, xs, x_dtype=oracle.DT[x_dtype], nthreads=16)
 
 
 def _bits(t):
@@ -120,3 +121,31 @@ def test_mx_random_shape_vs_oracle(case):
         one = U.q.mxfp4(w, s, xd[m:m + 1], out_dtype=torch.float32)
         torch.cuda.synchronize()
         assert torch.equal(_bits(y[m]), _bits(one[0])), f"vector {m}"
+
+
+F32_CASES = [  # N, K, Ms: fp32 activations (four vectors per launch)
+    (67, 2080, (1, 4, 5, 13)),   # wave-step tail; 5 and 13 vectors: balanced tiles
+    (300, 4096, (2, 3)),         # ragged row blocks
+    (200, 32768, (1, 4)),        # long K: one vector whole, four in K windows
+    (5, 65536, (1, 3)),          # the longest K: K windows even for one vector
+    (15360, 3840, (1, 13)),      # the up-projection shape
+]
+
+
+@pytest.mark.parametrize("case", F32_CASES, ids=lambda c: f"N{c[0]}_K{c[1]}")
+def test_mx_f32_x_vs_oracle(case):
+    N, K, Ms = case
+    p = gen.make_mx_problem(N, K, "f32", seed=N + K + 1)
+    w, s = _dev(p)
+    xs, xd = _x(p, max(Ms), "f32")
+    for M in Ms:
+        U.say(f"mxfp4 fp32 x N={N} K={K} M={M}")
+        y = U.q.mxfp4(w, s, xd[:M], out_dtype=torch.float32)
+        y16 = U.q.mxfp4(w, s, xd[:M], out_dtype=torch.bfloat16)
+        torch.cuda.synchronize()
+        U.check_parity(y, _ref(p, xs[:M], "f32"), f"mxfp4 fp32 x N={N} K={K} M={M}")
+        assert torch.equal(y16.view(torch.int16), U.rne_bf16(y).view(torch.int16))
+        for m in sorted({0, M // 2, M - 1}):
+            one = U.q.mxfp4(w, s, xd[m:m + 1], out_dtype=torch.float32)
+            torch.cuda.synchronize()
+            assert torch.equal(_bits(y[m]), _bits(one[0])), f"M={M} vector {m}"
