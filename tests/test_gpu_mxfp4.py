@@ -149,3 +149,30 @@ def test_mx_f32_x_vs_oracle(case):
             one = U.q.mxfp4(w, s, xd[m:m + 1], out_dtype=torch.float32)
             torch.cuda.synchronize()
             assert torch.equal(_bits(y[m]), _bits(one[0])), f"M={M} vector {m}"
+
+
+def _random_f32_cases(n=30, seed=4343):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        K = 32 * int(rng.integers(1, 513))
+        N = int(rng.integers(1, 321))
+        M = int(rng.choice([1, 2, 3, 4, 5, 8, 13]))
+        out.append((N, K, M, 7000 + i))
+    return out
+
+
+@pytest.mark.parametrize("case", _random_f32_cases(), ids=lambda c: f"N{c[0]}_K{c[1]}_M{c[2]}")
+def test_mx_f32_x_random_shape_vs_oracle(case):
+    # seeded random shapes with fp32 activations (K up to 16384, M up to 13)
+    N, K, M, seed = case
+    p = gen.make_mx_problem(N, K, "f32", seed=seed)
+    w, s = _dev(p)
+    xs, xd = _x(p, 13, "f32")
+    U.say(f"mxfp4 fp32 x random N={N} K={K} M={M}")
+    y = U.q.mxfp4(w, s, xd[:M], out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    U.check_parity(y, _ref(p, xs[:M], "f32"), f"mxfp4 fp32 x N={N} K={K} M={M}")
+    one = U.q.mxfp4(w, s, xd[M - 1:M], out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(y[M - 1]), _bits(one[0])), f"vector {M - 1}"
