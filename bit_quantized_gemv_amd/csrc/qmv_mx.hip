@@ -128,7 +128,8 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void qmv_mx_kernel(MxParams p)
     // the first weight step behind it.
     const int cwin = p.win_steps * kWave;                 // chunks per window
     constexpr int XB = XF32 ? 4 : 2;                      // activation bytes
-    constexpr int PPC = 32 * XB / 16;                     // 16-byte pieces per chunk
+    constexpr int PSH = XF32 ? 3 : 2;                     // log2 of 16-byte pieces per chunk
+    constexpr int PPC = 1 << PSH;
     constexpr int CB = 32 * XB;                           // LDS bytes per chunk
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(p.x, M * p.K * XB);
     auto stage = [&](int win, auto first_tag) {
@@ -140,7 +141,7 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void qmv_mx_kernel(MxParams p)
             for (int j = 0; j < 8; ++j) {
                 const int i = min(i0 + j * (int)blockDim.x + (int)threadIdx.x, items - 1);
                 const int m = i / (cwin * PPC), rem = i - m * (cwin * PPC);
-                const int c = min(c0 + rem / PPC, p.chunks - 1), piece = rem % PPC;
+                const int c = min(c0 + (rem >> PSH), p.chunks - 1), piece = rem & (PPC - 1);
                 v[j] = buf_load(xr, (m * p.K + c * 32) * XB + piece * 16);
             }
             if constexpr (decltype(with_issue)::value) issue(0, blockIdx.x, 0);
@@ -149,7 +150,7 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void qmv_mx_kernel(MxParams p)
                 const int i = i0 + j * (int)blockDim.x + (int)threadIdx.x;
                 if (i < items) {
                     const int m = i / (cwin * PPC), rem = i - m * (cwin * PPC);
-                    const int cl = rem / PPC, piece = rem % PPC;
+                    const int cl = rem >> PSH, piece = rem & (PPC - 1);
                     const uint4 d = (c0 + cl < p.chunks) ? v[j] : make_uint4(0, 0, 0, 0);
                     *reinterpret_cast<uint4*>(lds + m * p.xm_bytes + lds_phys(cl * CB + piece * 16)) = d;
                 }
