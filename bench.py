@@ -55,10 +55,10 @@ KERNEL_SOURCES = ("bit_quantized_gemv_amd/csrc/qmv_kernel.hpp",)
 MX_KERNEL_SOURCES = ("bit_quantized_gemv_amd/csrc/qmv_kernel.hpp", "bit_quantized_gemv_amd/csrc/qmv_mx.hip")
 
 
-def mx_bytes(N, K, M, y_bytes=2):
+def mx_bytes(N, K, M, y_bytes=2, x_bytes=2):
     """Algorithmic bytes of one mxfp4 call: E2M1 codes, one E8M0 byte per 32
-    values, bf16 x, the output."""
-    return N * K // 2 + N * (K // 32) + M * K * 2 + M * N * y_bytes
+    values, the activations (bf16 unless given), the output."""
+    return N * K // 2 + N * (K // 32) + M * K * x_bytes + M * N * y_bytes
 
 
 def alg_bytes(N, K, bits, gs, M, x_bytes=2, y_bytes=2, sb_bytes=2):
@@ -189,7 +189,8 @@ def _cpu_model():
 def workload_table(args, q, gen, torch, np, dev):
     """Every 12B/27B-class workload at M = 1, 2, 4, 8, 13: us per call (graph
     replay over rotating copies as in the bench line, median of three replays)
-    and the default launch; then the mxfp4 mode on the four projection shapes."""
+    and the default launch; then the mxfp4 mode on the four projection shapes,
+    with bf16 and with fp32 activations."""
     for name in ("up_4b_15360x3840", "down_4b_3840x15360", "up_2b_15360x3840",
                  "up_4b_17408x5120", "down_4b_5120x17408"):
         p = gen.make_problem(name)
@@ -226,20 +227,21 @@ def workload_table(args, q, gen, torch, np, dev):
         nc = max(2, -(-ROTATE_BYTES // mx_bytes(N, K, 13)))
         copies = [(torch.from_numpy(pm.w_packed.view(np.int32)).to(dev), torch.from_numpy(pm.scales).to(dev))
                   for _ in range(nc)]
-        xm = torch.from_numpy(pm.x.view(np.int16)).view(torch.bfloat16).to(dev)
+        xbf = torch.from_numpy(pm.x.view(np.int16)).view(torch.bfloat16).to(dev)
         ym = torch.empty(13, N, dtype=torch.bfloat16, device=dev)
+        for xm, x_dt, xb in ((xbf, q.DT_BF16, 2), (xbf.float(), q.DT_F32, 4)):
+            def launch_mx(i, M, stream, xm=xm, x_dt=x_dt):
+                st = q.mxfp4_ptr(copies[i][0].data_ptr(), copies[i][1].data_ptr(), xm.data_ptr(), ym.data_ptr(),
+                                 M, N, K, x_dt, q.DT_BF16, stream.cuda_stream)
+                if st != 0:
+                    raise q.QmvError(st, "qmv_mxfp4")
 
-        def launch_mx(i, M, stream):
-            st = q.mxfp4_ptr(copies[i][0].data_ptr(), copies[i][1].data_ptr(), xm.data_ptr(), ym.data_ptr(),
-                             M, N, K, q.DT_BF16, q.DT_BF16, stream.cuda_stream)
-            if st != 0:
-                raise q.QmvError(st, "qmv_mxfp4")
-
-        for M in (1, 2, 4, 8, 13):
-            us, _ = time_calls(launch_mx, nc, M, args.steps, args.warmup, torch, replays=3)
-            nb = mx_bytes(N, K, M)
-            print(json.dumps({"workload": f"mxfp4_{N}x{K}", "M": M, "us_per_call": round(us, 3),
-                              "GB/s": round(nb / (us * 1e-6) / 1e9, 1)}), flush=True)
+            for M in (1, 2, 4, 8, 13):
+                us, _ = time_calls(launch_mx, nc, M, args.steps, args.warmup, torch, replays=3)
+                nb = mx_bytes(N, K, M, x_bytes=xb)
+                print(json.dumps({"workload": f"mxfp4_{N}x{K}", "x": "f32" if xb == 4 else "bf16", "M": M,
+                                  "us_per_call": round(us, 3), "GB/s": round(nb / (us * 1e-6) / 1e9, 1)}),
+                      flush=True)
         del copies
         torch.cuda.empty_cache()
 
@@ -248,7 +250,9 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    # untimed calls before each measurement: 2000 (about 20 ms of GPU work) let the
+    # clocks settle; with 20 the first measurements of a process ran up to 10% slower
+    ap.add_argument("--warmup", type=int, default=2000)
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="time budget of the CPU-oracle baseline (0 = skip)")
     ap.add_argument("--calib-copy", action="store_true",
