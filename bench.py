@@ -249,7 +249,9 @@ def workload_table(args, q, gen, torch, np, dev):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    # timed calls per measurement, in one graph: 1000 spread the graph's own launch
+    # cost (about 20 us per replay) to ~0.02 us per call (~0.1 us at 200)
+    ap.add_argument("--steps", type=int, default=1000)
     # untimed calls before each measurement: 2000 (about 20 ms of GPU work) let the
     # clocks settle; with 20 the first measurements of a process ran up to 10% slower
     ap.add_argument("--warmup", type=int, default=2000)
