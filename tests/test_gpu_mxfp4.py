@@ -176,3 +176,46 @@ def test_mx_f32_x_random_shape_vs_oracle(case):
     one = U.q.mxfp4(w, s, xd[M - 1:M], out_dtype=torch.float32)
     torch.cuda.synchronize()
     assert torch.equal(_bits(y[M - 1]), _bits(one[0])), f"vector {M - 1}"
+
+
+def test_mx_graph_capture_replays_match_eager():
+    # mxfp4 calls captured in one HIP graph (bf16 x at M = 1 and 13, fp32 x at
+    # M = 5: two tiles): every replay, with new inputs and eager calls in
+    # between, equals the eager calls on the same inputs bit for bit.
+    p = gen.make_mx_problem(15360, 3840, "bf16", seed=4101)
+    w, s = _dev(p)
+    xs_b, xall_b = _x(p, 3 * 13)
+    xall_f = U.x_to_dev(gen.make_x(p.K, "f32", 4102, rows=3 * 5), "f32")
+    xin_b = xall_b[:13].clone()
+    xin_f = xall_f[:5].clone()
+    outs = [torch.empty(1, p.N, dtype=torch.float32, device=U.DEV),
+            torch.empty(13, p.N, dtype=torch.bfloat16, device=U.DEV),
+            torch.empty(5, p.N, dtype=torch.float32, device=U.DEV)]
+
+    def calls(stream):
+        U.q.mxfp4(w, s, xin_b[:1], out=outs[0], stream=stream)
+        U.q.mxfp4(w, s, xin_b, out=outs[1], stream=stream)
+        U.q.mxfp4(w, s, xin_f, out=outs[2], stream=stream)
+
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        calls(stream)                                                   # warm-up
+    stream.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        calls(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    for i in range(3):
+        U.say(f"mxfp4 graph replay {i}")
+        xb = xall_b[13 * i:13 * (i + 1)]
+        xf = xall_f[5 * i:5 * (i + 1)]
+        xin_b.copy_(xb)
+        xin_f.copy_(xf)
+        eager = [U.q.mxfp4(w, s, xb[:1], out_dtype=torch.float32),
+                 U.q.mxfp4(w, s, xb, out_dtype=torch.bfloat16),
+                 U.q.mxfp4(w, s, xf, out_dtype=torch.float32)]
+        g.replay()
+        torch.cuda.synchronize()
+        for j in range(3):
+            assert torch.equal(_bits(outs[j]), _bits(eager[j])), f"replay {i} call {j}"
