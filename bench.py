@@ -9,9 +9,12 @@ A step is one qmv call (the whole hot path: activation staging, weight and
 metadata streaming, decode, per-group dot and fold, reduction, output) over
 one copy of the inputs.  Inputs rotate over enough copies (>= 1 GiB) that the
 256 MB Infinity Cache cannot serve the weights, and are resident in HBM before
-timing starts.  The K timed calls are captured once in a HIP graph on the
-launch stream and replayed; HIP events on that stream bracket the replay, so
-the per-call time is (event time) / K.
+timing starts.  Before the first measurement the process runs untimed calls
+for at least 30 ms of GPU time (clocks settle), then each measurement runs its
+W warm-up calls and times graphs of K and of 2K calls on the launch stream
+between HIP events (median of 9 alternating replays each): the per-call time
+is (T(2K) - T(K)) / K, the time of K whole calls without the fixed cost of a
+graph replay.
 
 Algorithmic bytes per call = packed weights + scales + biases + activations +
 outputs, each counted once:
@@ -30,6 +33,13 @@ Prints one JSON line (the driver's contract) with extra objects:
                        up-projection (no launch)
     cpu_baseline    -- the CPU oracle on the machine's host cores (bounded sample),
                        and one of its calls on a single thread
+
+Other modes (one JSON line per point instead of the bench line):
+    --table          every 12B/27B-class workload at M = 1, 2, 4, 8, 13, and the
+                     mxfp4 mode on the four projection shapes
+    --sweep-rows     rows per wavefront 1-4 at M = 1, 4, 8, 13 on the 27B-class
+                     shapes, with VGPRs, LDS, grid and wavefronts per SIMD
+    --sweep-ceiling  the streaming-read ceiling over the launch shape
 """
 from __future__ import annotations
 
@@ -51,6 +61,7 @@ PEAK_GBS = 8000.0           # MI355X HBM3E
 # v_dot2_f32_bf16 (2 multiply-adds = 4 flops) per lane per cycle.
 PEAK_DOT_TFLOPS = 256 * 64 * 2.4e9 * 4 / 1e12
 ROTATE_BYTES = 1 << 30      # >= 4x the 256 MB Infinity Cache
+SETTLE_MS = 30.0            # untimed GPU work before the first measurement
 KERNEL_SOURCES = ("bit_quantized_gemv_amd/csrc/qmv_kernel.hpp",)
 MX_KERNEL_SOURCES = ("bit_quantized_gemv_amd/csrc/qmv_kernel.hpp", "bit_quantized_gemv_amd/csrc/qmv_mx.hip")
 
@@ -94,36 +105,71 @@ def traffic_for(M: int, name="qmv_up_4b_15360x3840_traffic.json", sources=KERNEL
     return None if e is None else e.get("hbm_bytes")
 
 
-def time_calls(launch, ncopies, M, steps, warmup, torch, replays=1):
-    """Per-call microseconds: K calls captured in one HIP graph, replayed
-    between HIP events on the capture/launch stream (the median of `replays`
-    timed replays; one for the bench line, which times exactly K calls)."""
+def settle_clocks(launch, ncopies, torch, min_ms=SETTLE_MS):
+    """Untimed calls until at least min_ms of GPU time has passed (clocks and
+    power state settle before the first measurement of a process, whatever
+    --warmup asks for)."""
+    stream = torch.cuda.Stream()
+    done_ms, calls = 0.0, 0
+    while done_ms < min_ms and calls < 200000:
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            start.record(stream)
+            for i in range(200):
+                launch((calls + i) % ncopies, 1, stream)
+            end.record(stream)
+        end.synchronize()
+        done_ms += start.elapsed_time(end)
+        calls += 200
+    return calls, done_ms
+
+
+def time_calls(launch, ncopies, M, steps, warmup, torch, replays=9):
+    """Per-call microseconds of `steps` calls, with the fixed cost of a graph
+    replay cancelled.
+
+    `warmup` untimed calls first; then two HIP graphs are captured on the
+    launch stream, one of K = steps calls and one of 2K calls (inputs rotating
+    over the copies), and replayed alternately `replays` times between HIP
+    events on that stream.  A replay costs its kernels plus a fixed launch
+    overhead (about 20 us here), so the difference of the median replay times,
+    T(2K) - T(K), is the time of K whole calls with that overhead removed; the
+    per-call time is that difference over K.  Returns (us per call, details)."""
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
         for i in range(warmup):
             launch(i % ncopies, M, stream)
     stream.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g, stream=stream):
-        for i in range(steps):
-            launch((warmup + i) % ncopies, M, torch.cuda.current_stream())
+
+    def capture(n, first):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(n):
+                launch((first + i) % ncopies, M, torch.cuda.current_stream())
+        return g
+
+    g1 = capture(steps, warmup)
+    g2 = capture(2 * steps, warmup + steps)
+    for g in (g1, g2):               # the first replay uploads the graph
+        g.replay()
     stream.synchronize()
-    g.replay()                       # first replay uploads the graph
-    stream.synchronize()
-    times = []
+    t1, t2 = [], []
     for _ in range(replays):
-        start = torch.cuda.Event(enable_timing=True)
-        end = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        with torch.cuda.stream(stream):
-            start.record(stream)
-            g.replay()
-            end.record(stream)
-        end.synchronize()
-        torch.cuda.synchronize()
-        times.append(start.elapsed_time(end))
-    ms = sorted(times)[len(times) // 2]
-    return ms * 1000.0 / steps, ms
+        for g, ts in ((g1, t1), (g2, t2)):
+            start = torch.cuda.Event(enable_timing=True)
+            end = torch.cuda.Event(enable_timing=True)
+            with torch.cuda.stream(stream):
+                start.record(stream)
+                g.replay()
+                end.record(stream)
+            end.synchronize()
+            ts.append(start.elapsed_time(end))
+    m1 = sorted(t1)[len(t1) // 2]
+    m2 = sorted(t2)[len(t2) // 2]
+    us = (m2 - m1) * 1000.0 / steps
+    return us, {"graph_K_ms": round(m1, 4), "graph_2K_ms": round(m2, 4),
+                "us_per_call_graph_K": round(m1 * 1000.0 / steps, 3)}
 
 
 def time_calls_eager(launch, ncopies, M, steps, torch):
@@ -186,40 +232,57 @@ def _cpu_model():
     return None
 
 
+def device_problem(p, torch, np, dev, ncopies, Mmax=13):
+    """`ncopies` device copies of a generated problem (weights, scales, biases,
+    13 activation vectors, output) as raw pointers, plus the tensors."""
+    base = [torch.from_numpy(p.w_packed.view(np.int32)).to(dev),
+            torch.from_numpy(p.scales.view(np.int16)).view(torch.bfloat16).to(dev),
+            torch.from_numpy(p.biases.view(np.int16)).view(torch.bfloat16).to(dev),
+            torch.from_numpy(p.x.view(np.int16)).view(torch.bfloat16).to(dev)]
+    copies = [[t.clone() for t in base] + [torch.empty(Mmax, p.N, dtype=torch.bfloat16, device=dev)]
+              for _ in range(ncopies)]
+    torch.cuda.synchronize()
+    ptrs = [tuple(t.data_ptr() for t in c) for c in copies]
+    return copies, ptrs
+
+
+def affine_launcher(q, p, ptrs, R=0):
+    N, K, bits, gs = p.N, p.K, p.bits, p.gs
+
+    def launch(i, M, stream):
+        w, s, b, x, y = ptrs[i]
+        st = q.affine_ptr(w, s, b, x, y, M, N, K, bits, gs, q.DT_BF16, q.DT_BF16, q.DT_BF16, R,
+                          stream.cuda_stream)
+        if st != 0:
+            raise q.QmvError(st, "qmv_affine_ex")
+    return launch
+
+
 def workload_table(args, q, gen, torch, np, dev):
-    """Every 12B/27B-class workload at M = 1, 2, 4, 8, 13: us per call (graph
-    replay over rotating copies as in the bench line, median of three replays)
-    and the default launch; then the mxfp4 mode on the four projection shapes,
-    with bf16 and with fp32 activations."""
+    """Every 12B/27B-class workload at M = 1, 2, 4, 8, 13: us per call (the
+    bench's timing: rotating copies, graphs of K and 2K calls) and the default
+    launch; then the mxfp4 mode on the four projection shapes, with bf16 and
+    with fp32 activations."""
+    settled = False
     for name in ("up_4b_15360x3840", "down_4b_3840x15360", "up_2b_15360x3840",
                  "up_4b_17408x5120", "down_4b_5120x17408"):
         p = gen.make_problem(name)
         N, K, bits, gs = p.N, p.K, p.bits, p.gs
-        per_copy = alg_bytes(N, K, bits, gs, 13)
-        nc = max(2, -(-ROTATE_BYTES // per_copy))
-        base = [torch.from_numpy(p.w_packed.view(np.int32)).to(dev),
-                torch.from_numpy(p.scales.view(np.int16)).view(torch.bfloat16).to(dev),
-                torch.from_numpy(p.biases.view(np.int16)).view(torch.bfloat16).to(dev),
-                torch.from_numpy(p.x.view(np.int16)).view(torch.bfloat16).to(dev)]
-        copies = [[t.clone() for t in base] + [torch.empty(13, N, dtype=torch.bfloat16, device=dev)]
-                  for _ in range(nc)]
-
-        def launch(i, M, stream):
-            w, s, b, x, y = (t.data_ptr() for t in copies[i])
-            st = q.affine_ptr(w, s, b, x, y, M, N, K, bits, gs, q.DT_BF16, q.DT_BF16, q.DT_BF16, 0,
-                              stream.cuda_stream)
-            if st != 0:
-                raise q.QmvError(st, "qmv_affine_ex")
-
+        nc = max(2, -(-ROTATE_BYTES // alg_bytes(N, K, bits, gs, 13)))
+        copies, ptrs = device_problem(p, torch, np, dev, nc)
+        launch = affine_launcher(q, p, ptrs)
+        if not settled:
+            settle_clocks(launch, nc, torch)
+            settled = True
         for M in (1, 2, 4, 8, 13):
-            us, _ = time_calls(launch, nc, M, args.steps, args.warmup, torch, replays=3)
+            us, _ = time_calls(launch, nc, M, args.steps, args.warmup, torch)
             nb = alg_bytes(N, K, bits, gs, M)
             inf = q.kernel_info(M, N, K, bits, gs)
             print(json.dumps({"workload": name, "M": M, "us_per_call": round(us, 3),
                               "GB/s": round(nb / (us * 1e-6) / 1e9, 1),
                               "rows_per_wave": inf["rows_per_wave"], "wg_size": inf["wg_size"],
                               "grid": inf["grid"], "k_windows": inf["k_windows"]}), flush=True)
-        del copies, base
+        del copies
         torch.cuda.empty_cache()
     # the mxfp4 mode on the same four projection shapes
     for N, K in ((15360, 3840), (3840, 15360), (17408, 5120), (5120, 17408)):
@@ -237,7 +300,7 @@ def workload_table(args, q, gen, torch, np, dev):
                     raise q.QmvError(st, "qmv_mxfp4")
 
             for M in (1, 2, 4, 8, 13):
-                us, _ = time_calls(launch_mx, nc, M, args.steps, args.warmup, torch, replays=3)
+                us, _ = time_calls(launch_mx, nc, M, args.steps, args.warmup, torch)
                 nb = mx_bytes(N, K, M, x_bytes=xb)
                 print(json.dumps({"workload": f"mxfp4_{N}x{K}", "x": "f32" if xb == 4 else "bf16", "M": M,
                                   "us_per_call": round(us, 3), "GB/s": round(nb / (us * 1e-6) / 1e9, 1)}),
@@ -246,15 +309,84 @@ def workload_table(args, q, gen, torch, np, dev):
         torch.cuda.empty_cache()
 
 
+def sweep_rows(args, q, gen, torch, np, dev):
+    """The 27B-class layer (17408 x 5120 and 5120 x 17408, 4-bit, group 64):
+    every rows-per-wavefront R in {1, 2, 3, 4} at M in {1, 4, 8, 13}, timed as
+    the bench line (the library's launch for that R), with the instance's
+    VGPRs, LDS per workgroup, grid and wavefronts per SIMD.  One JSON line per
+    point; `default` marks the R the library picks by itself."""
+    settled = False
+    for name in ("up_4b_17408x5120", "down_4b_5120x17408"):
+        p = gen.make_problem(name)
+        N, K, bits, gs = p.N, p.K, p.bits, p.gs
+        nc = max(2, -(-ROTATE_BYTES // alg_bytes(N, K, bits, gs, 13)))
+        copies, ptrs = device_problem(p, torch, np, dev, nc)
+        if not settled:
+            settle_clocks(affine_launcher(q, p, ptrs), nc, torch)
+            settled = True
+        for M in (1, 4, 8, 13):
+            r_default = q.kernel_info(M, N, K, bits, gs)["rows_per_wave"]
+            for R in (1, 2, 3, 4):
+                us, det = time_calls(affine_launcher(q, p, ptrs, R), nc, M, args.steps, args.warmup, torch)
+                inf = q.kernel_info(M, N, K, bits, gs, rows_per_wave=R)
+                nb = alg_bytes(N, K, bits, gs, M)
+                print(json.dumps({"sweep": "rows_per_wave", "workload": name, "M": M, "R": R,
+                                  "default": R == r_default, "us_per_call": round(us, 3),
+                                  "GB/s": round(nb / (us * 1e-6) / 1e9, 1),
+                                  "vgprs": inf["vgprs"], "scratch_bytes": inf["scratch_bytes"],
+                                  "lds_bytes": inf["lds_bytes"], "wg_size": inf["wg_size"],
+                                  "grid": inf["grid"], "waves_per_simd": inf["waves_per_simd"],
+                                  "k_windows": inf["k_windows"]}), flush=True)
+        del copies
+        torch.cuda.empty_cache()
+
+
+def sweep_ceiling(args, q, gen, torch, np, dev):
+    """The streaming-read ceiling over the bench line's byte count (33,216,000
+    B), same rotation and timing, swept over the launch shape: workgroups per
+    compute unit, wavefronts per workgroup, loads in flight per lane, and
+    contiguous or interleaved spans.  One JSON line per shape."""
+    p = gen.make_problem(WORKLOAD)
+    nb = alg_bytes(p.N, p.K, p.bits, p.gs, 1)
+    nc = max(2, -(-ROTATE_BYTES // nb))
+    bufs = [torch.empty(nb, dtype=torch.uint8, device=dev).random_(0, 256) for _ in range(nc)]
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    shape = [4, 8, 4, 0]
+
+    def launch(i, M, stream):
+        st = q.stream_read_ex_ptr(bufs[i].data_ptr(), nb, sink.data_ptr(), *shape,
+                                  stream=stream.cuda_stream)
+        if st != 0:
+            raise q.QmvError(st, "qmv_stream_read_ex")
+
+    settle_clocks(launch, nc, torch)
+    best = None
+    for wg in (1, 2, 4, 8, 16):
+        for waves in (4, 8, 16):
+            if wg * waves > 32 * 4:
+                continue
+            for batch in (1, 2, 4, 8, 16):
+                for inter in (0, 1):
+                    shape[:] = [wg, waves, batch, inter]
+                    us, _ = time_calls(launch, nc, 1, args.steps, args.warmup, torch)
+                    gbs = nb / (us * 1e-6) / 1e9
+                    rec = {"sweep": "stream_ceiling", "bytes": nb, "wg_per_cu": wg, "waves_per_wg": waves,
+                           "batch": batch, "interleave": inter, "us_per_call": round(us, 3),
+                           "GB/s": round(gbs, 1), "frac_of_peak": round(gbs / PEAK_GBS, 4)}
+                    print(json.dumps(rec), flush=True)
+                    if best is None or us < best["us_per_call"]:
+                        best = rec
+    print(json.dumps({"sweep": "stream_ceiling_best", **best}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    # timed calls per measurement, in one graph: 1000 spread the graph's own launch
-    # cost (about 20 us per replay) to ~0.02 us per call (~0.1 us at 200)
-    ap.add_argument("--steps", type=int, default=1000)
-    # untimed calls before each measurement: 2000 (about 20 ms of GPU work) let the
-    # clocks settle; with 20 the first measurements of a process ran up to 10% slower
-    ap.add_argument("--warmup", type=int, default=2000)
+    # K: calls per timed graph (graphs of K and 2K calls are timed; their
+    # difference cancels the graph's fixed launch cost)
+    ap.add_argument("--steps", type=int, default=200)
+    # untimed calls before each measurement (after the process-wide clock settling)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="time budget of the CPU-oracle baseline (0 = skip)")
     ap.add_argument("--calib-copy", action="store_true",
@@ -262,6 +394,11 @@ def main():
     ap.add_argument("--table", action="store_true",
                     help="instead of the bench line, time every workload at M = 1, 2, 4, 8, 13 with "
                          "the library's default launch (one JSON line per case)")
+    ap.add_argument("--sweep-rows", action="store_true",
+                    help="instead of the bench line, time rows per wavefront 1-4 at M = 1, 4, 8, 13 on "
+                         "the 27B-class shapes, with resources and occupancy per point")
+    ap.add_argument("--sweep-ceiling", action="store_true",
+                    help="instead of the bench line, sweep the streaming-read ceiling's launch shape")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -279,32 +416,22 @@ def main():
     if args.table:
         workload_table(args, q, gen, torch, np, dev)
         return
+    if args.sweep_rows:
+        sweep_rows(args, q, gen, torch, np, dev)
+        return
+    if args.sweep_ceiling:
+        sweep_ceiling(args, q, gen, torch, np, dev)
+        return
     wl = gen.WORKLOADS[WORKLOAD]
     p = gen.make_problem(WORKLOAD)
     N, K, bits, gs = p.N, p.K, p.bits, p.gs
     Mmax = 13
-
-    w0 = torch.from_numpy(p.w_packed.view(np.int32)).to(dev)
-    s0 = torch.from_numpy(p.scales.view(np.int16)).view(torch.bfloat16).to(dev)
-    b0 = torch.from_numpy(p.biases.view(np.int16)).view(torch.bfloat16).to(dev)
-    x0 = torch.from_numpy(p.x.view(np.int16)).view(torch.bfloat16).to(dev)
     per_copy = alg_bytes(N, K, bits, gs, Mmax)
     ncopies = max(2, -(-ROTATE_BYTES // per_copy))
-    W = [w0.clone() for _ in range(ncopies)]
-    S = [s0.clone() for _ in range(ncopies)]
-    B = [b0.clone() for _ in range(ncopies)]
-    X = [x0.clone() for _ in range(ncopies)]
-    Y = [torch.empty(Mmax, N, dtype=torch.bfloat16, device=dev) for _ in range(ncopies)]
-    ptrs = [(W[i].data_ptr(), S[i].data_ptr(), B[i].data_ptr(), X[i].data_ptr(), Y[i].data_ptr())
-            for i in range(ncopies)]
-    torch.cuda.synchronize()
-
-    def launch(i, M, stream):
-        w, s, b, x, y = ptrs[i]
-        st = q.affine_ptr(w, s, b, x, y, M, N, K, bits, gs, q.DT_BF16, q.DT_BF16, q.DT_BF16, 0,
-                          stream.cuda_stream)
-        if st != 0:
-            raise q.QmvError(st, "qmv_affine_ex")
+    copies, ptrs = device_problem(p, torch, np, dev, ncopies)
+    X = [c[3] for c in copies]
+    Y = [c[4] for c in copies]
+    launch = affine_launcher(q, p, ptrs)
 
     # correctness guard on the timed configuration: M=13 vector 0 == M=1 call
     launch(0, 1, torch.cuda.current_stream())
@@ -313,13 +440,14 @@ def main():
     torch.cuda.synchronize()
     assert torch.equal(Y[0][0], y1), "M-invariance violated on the bench workload"
 
+    settle_calls, settle_ms = settle_clocks(launch, ncopies, torch)
     results = {}
     for M in (1, Mmax):
-        us, total_ms = time_calls(launch, ncopies, M, args.steps, args.warmup, torch)
+        us, det = time_calls(launch, ncopies, M, args.steps, args.warmup, torch)
         us_eager = time_calls_eager(launch, ncopies, M, args.steps, torch)
         nb = alg_bytes(N, K, bits, gs, M)
         info = q.kernel_info(M, N, K, bits, gs)
-        results[M] = dict(us=us, total_ms=total_ms, us_eager=us_eager, bytes=nb,
+        results[M] = dict(us=us, det=det, us_eager=us_eager, bytes=nb,
                           gbs=nb / (us * 1e-6) / 1e9, info=info)
 
     # streaming-read ceiling over the M=1 call's byte count, same rotation and timing
@@ -383,6 +511,11 @@ def main():
 
     r1, r13 = results[1], results[Mmax]
     flops13 = 2 * Mmax * N * K
+    timing = (f"per call = (T(2K) - T(K)) / K: HIP graphs of K = {args.steps} and {2 * args.steps} calls "
+              f"(inputs rotating over {ncopies} copies) replayed alternately 9 times each between HIP "
+              f"events on the launch stream, medians; {args.warmup} untimed calls before each "
+              f"measurement, and {settle_calls} untimed calls ({settle_ms:.0f} ms of GPU time) before "
+              f"the first")
     out = {
         "metric": METRIC,
         "value": round(r1["gbs"], 1),
@@ -390,7 +523,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(r1["total_ms"] / args.steps, 6),
+        "ms_per_step": round(r1["us"] / 1000.0, 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -399,10 +532,10 @@ def main():
         "config": {"workload": WORKLOAD, "N": N, "K": K, "bits": bits, "group_size": gs, "M": 1,
                    "x": "bf16", "scales_biases": "bf16", "y": "bf16", "accumulate": "f32",
                    "rotation_copies": ncopies, "rotation_bytes": ncopies * per_copy,
-                   "timing": "HIP graph of K calls replayed between HIP events on the launch stream",
-                   "seed": wl["seed"]},
+                   "timing": timing, "seed": wl["seed"]},
         "us_per_call": round(r1["us"], 3),
         "pct_of_hbm_peak": round(100.0 * r1["gbs"] / PEAK_GBS, 2),
+        "timing_detail": r1["det"],
         "us_per_call_eager": round(r1["us_eager"], 3),
         "kernel": r1["info"],
         "roofline": {
@@ -416,6 +549,7 @@ def main():
         },
         "stream_ceiling": {
             "bytes": nb1,
+            "shape": "4 workgroups of 8 wavefronts per CU, 4 loads in flight per lane",
             "us_per_call": round(us_stream, 3),
             "GB/s": round(gbs_stream, 1),
             "frac_of_peak": round(gbs_stream / PEAK_GBS, 4),
@@ -429,6 +563,7 @@ def main():
             "GB/s": round(r13["gbs"], 1),
             "pct_of_hbm_peak": round(100.0 * r13["gbs"] / PEAK_GBS, 2),
             "alg_bytes_per_launch": r13["bytes"],
+            "timing_detail": r13["det"],
             "us_per_call_eager": round(r13["us_eager"], 3),
             "valu_TFLOPs_dot": round(flops13 / (r13["us"] * 1e-6) / 1e12, 2),
             "roofline_alu": {

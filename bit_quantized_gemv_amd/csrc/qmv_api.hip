@@ -57,25 +57,25 @@ int check_args(const uint32_t* w, const void* s, const void* b, const void* x, v
     return QMV_OK;
 }
 
-int pf_index(int PF) { return PF == 1 ? 0 : (PF == 2 ? 1 : 2); }
-
+// Kernel instance for (bits, group size, activation and scale/bias dtypes,
+// rows per wavefront, vectors, K windows); every instance keeps one unit in
+// flight per wavefront.
 KernelFn pick_kernel(int bits, int gs, bool xf32, bool sbf, int R, int PF, int M, bool win)
 {
+    if (PF != 1) return nullptr;
     const int ri = r_index(R);
-    const int pi = pf_index(PF);
     const int mi = M - 1;
     const int si = sbf ? 1 : 0;
     if (win) {
-        if (PF != 1) return nullptr;
         if (bits == 4 && gs == 64) return xf32 ? qmv::qmv_wtable_b4_g64_f32[ri][mi][si] : qmv::qmv_wtable_b4_g64_bf16[ri][mi][si];
         if (bits == 4 && gs == 128) return xf32 ? qmv::qmv_wtable_b4_g128_f32[ri][mi][si] : qmv::qmv_wtable_b4_g128_bf16[ri][mi][si];
         if (bits == 2 && gs == 64) return xf32 ? qmv::qmv_wtable_b2_g64_f32[ri][mi][si] : qmv::qmv_wtable_b2_g64_bf16[ri][mi][si];
         return xf32 ? qmv::qmv_wtable_b2_g128_f32[ri][mi][si] : qmv::qmv_wtable_b2_g128_bf16[ri][mi][si];
     }
-    if (bits == 4 && gs == 64) return xf32 ? qmv::qmv_table_b4_g64_f32[ri][pi][mi][si] : qmv::qmv_table_b4_g64_bf16[ri][pi][mi][si];
-    if (bits == 4 && gs == 128) return xf32 ? qmv::qmv_table_b4_g128_f32[ri][pi][mi][si] : qmv::qmv_table_b4_g128_bf16[ri][pi][mi][si];
-    if (bits == 2 && gs == 64) return xf32 ? qmv::qmv_table_b2_g64_f32[ri][pi][mi][si] : qmv::qmv_table_b2_g64_bf16[ri][pi][mi][si];
-    return xf32 ? qmv::qmv_table_b2_g128_f32[ri][pi][mi][si] : qmv::qmv_table_b2_g128_bf16[ri][pi][mi][si];
+    if (bits == 4 && gs == 64) return xf32 ? qmv::qmv_table_b4_g64_f32[ri][mi][si] : qmv::qmv_table_b4_g64_bf16[ri][mi][si];
+    if (bits == 4 && gs == 128) return xf32 ? qmv::qmv_table_b4_g128_f32[ri][mi][si] : qmv::qmv_table_b4_g128_bf16[ri][mi][si];
+    if (bits == 2 && gs == 64) return xf32 ? qmv::qmv_table_b2_g64_f32[ri][mi][si] : qmv::qmv_table_b2_g64_bf16[ri][mi][si];
+    return xf32 ? qmv::qmv_table_b2_g128_f32[ri][mi][si] : qmv::qmv_table_b2_g128_bf16[ri][mi][si];
 }
 
 struct Plan {
@@ -361,11 +361,19 @@ int qmv_affine_ex(const uint32_t* w_packed, const void* scales, const void* bias
     const bool sbf = (sb_dt == QMV_DT_BF16);
     const int mc = tile_vectors(M, N, K, bits, group_size, xf32, sbf, rows_per_wave);
     if (mc < 1) return QMV_E_SHAPE;
-    for (int m0 = 0; m0 < M; m0 += mc) {
-        const int mm = std::min(mc, M - m0);
-        Plan pl;
-        st = choose_plan(mm, N, K, bits, group_size, xf32, sbf, rows_per_wave, pl);
+    // Tiles of mc vectors and, when M is not a multiple of mc, one last tile
+    // of M % mc: both plans are made before the first launch is enqueued, so a
+    // plan that fails leaves y untouched.
+    const int last = M % mc;
+    Plan plans[2];
+    st = choose_plan(mc, N, K, bits, group_size, xf32, sbf, rows_per_wave, plans[0]);
+    if (st != QMV_OK) return st;
+    if (last != 0) {
+        st = choose_plan(last, N, K, bits, group_size, xf32, sbf, rows_per_wave, plans[1]);
         if (st != QMV_OK) return st;
+    }
+    for (int m0 = 0; m0 < M; m0 += mc) {
+        Plan& pl = plans[(M - m0 < mc) ? 1 : 0];
         Params& p = pl.p;
         p.w = w_packed;
         p.s = static_cast<const uint16_t*>(scales);
@@ -390,7 +398,7 @@ int qmv_affine(const uint32_t* w_packed, const void* scales, const void* biases,
 }
 
 int qmv_kernel_info(int M, int N, int K, int bits, int group_size, qmv_dtype x_dt,
-                    int rows_per_wave, qmv_kernel_info_t* out)
+                    qmv_dtype sb_dt, qmv_dtype y_dt, int rows_per_wave, qmv_kernel_info_t* out)
 {
     if (!out) return QMV_E_NULL;
     // validate the shape with stand-in aligned, non-overlapping pointers
@@ -399,13 +407,14 @@ int qmv_kernel_info(int M, int N, int K, int bits, int group_size, qmv_dtype x_d
     int st = check_args(reinterpret_cast<const uint32_t*>(base), reinterpret_cast<const void*>(base + stride),
                         reinterpret_cast<const void*>(base + 2 * stride), reinterpret_cast<const void*>(base + 3 * stride),
                         reinterpret_cast<void*>(base + 4 * stride), M, N, K, bits, group_size, x_dt,
-                        QMV_DT_BF16, QMV_DT_F32, rows_per_wave);
+                        sb_dt, y_dt, rows_per_wave);
     if (st != QMV_OK) return st;
     const bool xf32 = (x_dt == QMV_DT_F32);
-    const int mc = tile_vectors(M, N, K, bits, group_size, xf32, true, rows_per_wave);
+    const bool sbf = (sb_dt == QMV_DT_BF16);
+    const int mc = tile_vectors(M, N, K, bits, group_size, xf32, sbf, rows_per_wave);
     if (mc < 1) return QMV_E_SHAPE;
     Plan pl;
-    st = choose_plan(mc, N, K, bits, group_size, xf32, true, rows_per_wave, pl);
+    st = choose_plan(mc, N, K, bits, group_size, xf32, sbf, rows_per_wave, pl);
     if (st != QMV_OK) return st;
     hipFuncAttributes attr;
     if (hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(pl.fn)) != hipSuccess) return QMV_E_LAUNCH;
@@ -414,7 +423,12 @@ int qmv_kernel_info(int M, int N, int K, int bits, int group_size, qmv_dtype x_d
     out->lds_bytes = pl.lds;
     out->wg_size = pl.W * qmv::kWave;
     out->grid = pl.grid;
-    out->waves_per_simd = std::min(pl.blocks_per_cu, (pl.grid + 255) / 256) * pl.W / 4;
+    // workgroups on the busiest compute unit (at most the resident count),
+    // times their wavefronts, over the four SIMDs of a compute unit
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return QMV_E_LAUNCH;
+    const int cus = cu_count(dev);
+    out->waves_per_simd = (std::min(pl.blocks_per_cu, (pl.grid + cus - 1) / cus) * pl.W + 3) / 4;
     out->rows_per_wave = pl.R;
     out->k_windows = pl.p.nwin;
     out->prefetch_units = pl.PF;

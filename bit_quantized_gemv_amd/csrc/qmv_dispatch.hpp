@@ -1,8 +1,8 @@
 // qmv_dispatch.hpp -- host-side tables of kernel instances, indexed by
-// (bits, group size, activation dtype) -> [rows per wavefront][prefetch
-// depth][M - 1][scale/bias dtype] for the instances that stage the whole K
-// at once, and -> [rows per wavefront][M - 1][scale/bias dtype] for the
-// K-windowed instances (one unit in flight).  Entries not instantiated are null.
+// (bits, group size, activation dtype) -> [rows per wavefront][M - 1][scale/bias
+// dtype], one table for the instances that stage the whole K at once and one
+// for the K-windowed instances (both keep one unit in flight per wavefront).
+// Entries not instantiated are null.
 #pragma once
 
 #include "qmv_kernel.hpp"
@@ -11,19 +11,17 @@ namespace qmv {
 
 using KernelFn = void (*)(Params);
 constexpr int kNumR = 4;      // rows per wavefront 1, 2, 3, 4
-constexpr int kNumPF = 3;     // units in flight per wavefront 1, 2, 4
 constexpr int kMaxM = 13;
 constexpr int kNumSb = 2;     // scales/biases fp16, bf16
-constexpr int kMaxMDeep = 4;  // prefetch depths above 1 exist for M <= 4 only
 
-extern const KernelFn qmv_table_b4_g64_bf16[kNumR][kNumPF][kMaxM][kNumSb];
-extern const KernelFn qmv_table_b4_g64_f32[kNumR][kNumPF][kMaxM][kNumSb];
-extern const KernelFn qmv_table_b4_g128_bf16[kNumR][kNumPF][kMaxM][kNumSb];
-extern const KernelFn qmv_table_b4_g128_f32[kNumR][kNumPF][kMaxM][kNumSb];
-extern const KernelFn qmv_table_b2_g64_bf16[kNumR][kNumPF][kMaxM][kNumSb];
-extern const KernelFn qmv_table_b2_g64_f32[kNumR][kNumPF][kMaxM][kNumSb];
-extern const KernelFn qmv_table_b2_g128_bf16[kNumR][kNumPF][kMaxM][kNumSb];
-extern const KernelFn qmv_table_b2_g128_f32[kNumR][kNumPF][kMaxM][kNumSb];
+extern const KernelFn qmv_table_b4_g64_bf16[kNumR][kMaxM][kNumSb];
+extern const KernelFn qmv_table_b4_g64_f32[kNumR][kMaxM][kNumSb];
+extern const KernelFn qmv_table_b4_g128_bf16[kNumR][kMaxM][kNumSb];
+extern const KernelFn qmv_table_b4_g128_f32[kNumR][kMaxM][kNumSb];
+extern const KernelFn qmv_table_b2_g64_bf16[kNumR][kMaxM][kNumSb];
+extern const KernelFn qmv_table_b2_g64_f32[kNumR][kMaxM][kNumSb];
+extern const KernelFn qmv_table_b2_g128_bf16[kNumR][kMaxM][kNumSb];
+extern const KernelFn qmv_table_b2_g128_f32[kNumR][kMaxM][kNumSb];
 
 extern const KernelFn qmv_wtable_b4_g64_bf16[kNumR][kMaxM][kNumSb];
 extern const KernelFn qmv_wtable_b4_g64_f32[kNumR][kMaxM][kNumSb];

@@ -418,6 +418,8 @@ int mx_check(const uint32_t* w, const uint8_t* s, const void* x, void* y, int M,
     const size_t nx = (size_t)M * (size_t)K * (x_dt == QMV_DT_F32 ? 4 : 2), ny = (size_t)M * (size_t)N * yb;
     if (overlap_mx(y, ny, w, nw) || overlap_mx(y, ny, s, ns) || overlap_mx(y, ny, x, nx))
         return QMV_E_ALIAS;
+    // the kernel's row offsets are 32-bit
+    if (nw >= (size_t)1 << 31) return QMV_E_SHAPE;
     return QMV_OK;
 }
 
@@ -438,18 +440,25 @@ extern "C" int qmv_mxfp4(const uint32_t* w_packed, const uint8_t* scales, const 
     const int step_bytes = mx_step_bytes(xf32);
     const MxShape shape = mx_shape(M, N, K, cus, xf32);
     const int tiles = (M + shape.per_launch - 1) / shape.per_launch;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    int m0 = 0;
-    for (int t = 0; t < tiles; ++t) {
-        // balanced tiles: the first M % tiles get one more vector
-        const int Mt = M / tiles + (t < M % tiles ? 1 : 0);
+    // Balanced tiles: the first M % tiles get one more vector, so there are at
+    // most two tile sizes.  Both launches are planned (instance, LDS,
+    // residency) before the first one is enqueued, so a refused plan leaves y
+    // untouched.
+    struct MxLaunch {
+        qmv::MxParams p;
+        MxKernelFn fn;
+        int lds, grid;
+    };
+    MxLaunch plans[2];
+    const int sizes[2] = {M / tiles + (M % tiles ? 1 : 0), M / tiles};
+    for (int i = 0; i < 2; ++i) {
+        const int Mt = sizes[i];
+        if (Mt < 1) continue;
         const bool win = shape.win_steps > 0 && Mt * mx_steps(K) * step_bytes > kMxLds;
         const int R = xf32 ? 2 : mx_rows(Mt, N, cus, win);
-        qmv::MxParams p;
+        qmv::MxParams& p = plans[i].p;
         p.w = w_packed;
         p.s = scales;
-        p.x = static_cast<const uint8_t*>(x) + (size_t)m0 * K * xb;
-        p.y = static_cast<uint8_t*>(y) + (size_t)m0 * N * yb;
         p.N = N;
         p.K = K;
         p.chunks = K / 32;
@@ -471,12 +480,21 @@ extern "C" int qmv_mxfp4(const uint32_t* w_packed, const uint8_t* scales, const 
         // workgroup for every compute unit
         int per = (p.n_rb + nb * cus - 1) / (nb * cus);
         if (Mt <= 2 && per == 1 && p.n_rb >= 2 * cus) per = 2;
-        const int grid = (p.n_rb + per - 1) / per;
-        // the kernel's row offsets are 32-bit
-        if ((size_t)N * (size_t)p.row_bytes >= (size_t)1 << 31) return QMV_E_SHAPE;
-        void* args[] = {&p};
-        if (hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3(grid), dim3(kMxW * qmv::kWave), args,
-                            (size_t)lds, s) != hipSuccess)
+        plans[i].fn = fn;
+        plans[i].lds = lds;
+        plans[i].grid = (p.n_rb + per - 1) / per;
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int m0 = 0;
+    for (int t = 0; t < tiles; ++t) {
+        const int i = (t < M % tiles || M % tiles == 0) ? 0 : 1;
+        const int Mt = sizes[i];
+        MxLaunch& L = plans[i];
+        L.p.x = static_cast<const uint8_t*>(x) + (size_t)m0 * K * xb;
+        L.p.y = static_cast<uint8_t*>(y) + (size_t)m0 * N * yb;
+        void* args[] = {&L.p};
+        if (hipLaunchKernel(reinterpret_cast<const void*>(L.fn), dim3(L.grid), dim3(kMxW * qmv::kWave), args,
+                            (size_t)L.lds, s) != hipSuccess)
             return QMV_E_LAUNCH;
         m0 += Mt;
     }

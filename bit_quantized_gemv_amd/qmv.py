@@ -47,12 +47,14 @@ def lib():
         L.qmv_affine.restype = I
         L.qmv_affine_ex.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, I, I, P]
         L.qmv_affine_ex.restype = I
-        L.qmv_kernel_info.argtypes = [I, I, I, I, I, I, I, ctypes.POINTER(KernelInfo)]
+        L.qmv_kernel_info.argtypes = [I, I, I, I, I, I, I, I, I, ctypes.POINTER(KernelInfo)]
         L.qmv_kernel_info.restype = I
         L.qmv_status_string.argtypes = [I]
         L.qmv_status_string.restype = ctypes.c_char_p
         L.qmv_stream_read.argtypes = [P, ctypes.c_longlong, P, I, P]
         L.qmv_stream_read.restype = I
+        L.qmv_stream_read_ex.argtypes = [P, ctypes.c_longlong, P, I, I, I, I, I, P]
+        L.qmv_stream_read_ex.restype = I
         L.qmv_mxfp4.argtypes = [P, P, P, P, I, I, I, I, I, P]
         L.qmv_mxfp4.restype = I
         _lib = L
@@ -77,6 +79,13 @@ def stream_read_ptr(buf, nbytes, out, checksum=False, stream=0) -> int:
     return lib().qmv_stream_read(buf, nbytes, out, 1 if checksum else 0, stream)
 
 
+def stream_read_ex_ptr(buf, nbytes, out, wg_per_cu, waves_per_wg, batch, interleave=0,
+                      checksum=False, stream=0) -> int:
+    """The streaming-read ceiling kernel with an explicit launch shape."""
+    return lib().qmv_stream_read_ex(buf, nbytes, out, 1 if checksum else 0, wg_per_cu,
+                                    waves_per_wg, batch, interleave, stream)
+
+
 def mxfp4_ptr(w, s, x, y, M, N, K, x_dt=DT_BF16, y_dt=DT_BF16, stream=0) -> int:
     """Raw C-ABI call of the mxfp4 mode with integer device pointers; returns
     the status code."""
@@ -89,29 +98,29 @@ def mxfp4(w, scales, x, *, out=None, out_dtype=None, stream=None):
     w: int32/uint32 [N][K/8] packed E2M1 codes (field 0 in the low bits);
     scales: uint8 [N][K/32] E8M0 block scales; x: bf16 or fp32 [M][K] (or [K]); out:
     optional fp32/bf16 [M][N] tensor, else allocated with out_dtype (default
-    bf16).
+    bf16).  Shapes, dtypes and devices are checked here (ValueError /
+    TypeError) before the call: the C ABI sees only pointers.
     """
     import torch
     squeeze = x.dim() == 1
     if squeeze:
         x = x.unsqueeze(0)
-    for t, n in ((w, "w"), (scales, "scales"), (x, "x")):
-        if not t.is_cuda:
-            raise ValueError(f"{n} must be a CUDA (HIP) tensor")
-        if not t.is_contiguous():
-            raise ValueError(f"{n} must be contiguous")
     if w.dtype not in (torch.int32, torch.uint32):
         raise TypeError("w must be int32 or uint32 packed words")
     if scales.dtype != torch.uint8:
         raise TypeError("scales must be uint8 (E8M0)")
     if x.dtype not in (torch.bfloat16, torch.float32):
         raise TypeError("x must be bf16 or fp32")
+    if x.dim() != 2 or w.dim() != 2:
+        raise ValueError("x must be [M][K] (or [K]) and w [N][K/8]")
     M, K = x.shape
     N = w.shape[0]
-    if out is None:
-        out = torch.empty((M, N), dtype=out_dtype or torch.bfloat16, device=x.device)
-    elif not out.is_contiguous() or tuple(out.shape) != (M, N):
-        raise ValueError("out must be a contiguous [M][N] tensor")
+    if K % 32 != 0:
+        raise ValueError(f"K = {K} is not a multiple of 32")
+    _expect(w, (N, K // 8), "w")
+    _expect(scales, (N, K // 32), "scales")
+    _check_tensors(((w, "w"), (scales, "scales"), (x, "x")))
+    out = _out_for(out, out_dtype, M, N, x, torch)
     st = torch.cuda.current_stream(x.device) if stream is None else stream
     status = mxfp4_ptr(w.data_ptr(), scales.data_ptr(), x.data_ptr(), out.data_ptr(), M, N, K,
                        _dt_of(x, "x"), _dt_of(out, "out"), st.cuda_stream)
@@ -138,27 +147,32 @@ def affine(w, scales, biases, x, *, bits: int, group_size: int, out=None, out_dt
     w: int32/uint32 [N][K*bits/32] packed codes (field 0 in the low bits);
     scales, biases: fp16 or bf16 [N][K/group_size]; x: fp32 or bf16 [M][K]
     (or [K]); out: optional fp32/bf16 [M][N] tensor, else allocated with
-    out_dtype (default bf16).
+    out_dtype (default bf16).  Shapes, dtypes and devices are checked here
+    (ValueError / TypeError) before the call: the C ABI sees only pointers.
     """
     import torch
     squeeze = x.dim() == 1
     if squeeze:
         x = x.unsqueeze(0)
-    for t, n in ((w, "w"), (scales, "scales"), (biases, "biases"), (x, "x")):
-        if not t.is_cuda:
-            raise ValueError(f"{n} must be a CUDA (HIP) tensor")
-        if not t.is_contiguous():
-            raise ValueError(f"{n} must be contiguous")
     if w.dtype not in (torch.int32, torch.uint32):
         raise TypeError("w must be int32 or uint32 packed words")
     if scales.dtype != biases.dtype:
         raise TypeError("scales and biases must share a dtype")
+    if bits not in (2, 4):
+        raise ValueError(f"bits must be 2 or 4, got {bits}")
+    if group_size not in (64, 128):
+        raise ValueError(f"group_size must be 64 or 128, got {group_size}")
+    if x.dim() != 2 or w.dim() != 2:
+        raise ValueError("x must be [M][K] (or [K]) and w [N][K*bits/32]")
     M, K = x.shape
     N = w.shape[0]
-    if out is None:
-        out = torch.empty((M, N), dtype=out_dtype or torch.bfloat16, device=x.device)
-    elif not out.is_contiguous() or tuple(out.shape) != (M, N):
-        raise ValueError("out must be a contiguous [M][N] tensor")
+    if K % group_size != 0:
+        raise ValueError(f"K = {K} is not a multiple of group_size = {group_size}")
+    _expect(w, (N, K * bits // 32), "w")
+    _expect(scales, (N, K // group_size), "scales")
+    _expect(biases, (N, K // group_size), "biases")
+    _check_tensors(((w, "w"), (scales, "scales"), (biases, "biases"), (x, "x")))
+    out = _out_for(out, out_dtype, M, N, x, torch)
     st = torch.cuda.current_stream(x.device) if stream is None else stream
     status = affine_ptr(w.data_ptr(), scales.data_ptr(), biases.data_ptr(), x.data_ptr(),
                         out.data_ptr(), M, N, K, bits, group_size, _dt_of(x, "x"),
@@ -169,9 +183,39 @@ def affine(w, scales, biases, x, *, bits: int, group_size: int, out=None, out_dt
     return out[0] if squeeze else out
 
 
-def kernel_info(M, N, K, bits, group_size, x_dt=DT_BF16, rows_per_wave=0) -> dict:
+def _check_tensors(named):
+    """Every tensor on one HIP device and contiguous."""
+    dev = None
+    for t, n in named:
+        if not t.is_cuda:
+            raise ValueError(f"{n} must be a CUDA (HIP) tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{n} must be contiguous")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{n} is on {t.device}, the other inputs on {dev}")
+
+
+def _expect(t, shape, name):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _out_for(out, out_dtype, M, N, x, torch):
+    if out is None:
+        return torch.empty((M, N), dtype=out_dtype or torch.bfloat16, device=x.device)
+    if not out.is_cuda or out.device != x.device:
+        raise ValueError("out must be on the inputs' device")
+    if not out.is_contiguous() or tuple(out.shape) != (M, N):
+        raise ValueError("out must be a contiguous [M][N] tensor")
+    return out
+
+
+def kernel_info(M, N, K, bits, group_size, x_dt=DT_BF16, sb_dt=DT_BF16, y_dt=DT_BF16,
+                rows_per_wave=0) -> dict:
     info = KernelInfo()
-    status = lib().qmv_kernel_info(M, N, K, bits, group_size, x_dt, rows_per_wave,
+    status = lib().qmv_kernel_info(M, N, K, bits, group_size, x_dt, sb_dt, y_dt, rows_per_wave,
                                    ctypes.byref(info))
     if status != 0:
         raise QmvError(status, "qmv_kernel_info")

@@ -45,10 +45,17 @@
  * 2-bit codes and large M), a call is issued as several launches on the same
  * stream, each over a subset of the vectors; the results do not change.
  *
- * Errors.  Arguments are validated on the host before anything is enqueued;
- * on any non-zero status nothing was launched and y is untouched.  A HIP
- * launch failure returns QMV_E_LAUNCH.  Faults inside a kernel surface, as
- * with any HIP kernel, at the caller's next synchronization.
+ * Errors.  Arguments are validated, and every launch of the call (one per
+ * tile of vectors, below) is planned, on the host before anything is
+ * enqueued; a status other than QMV_OK from validation or planning means that
+ * nothing was launched and y is untouched.  QMV_E_LAUNCH from the HIP runtime
+ * refusing a launch is the one exception: in a call cut into several tiles,
+ * the tiles enqueued before the refused one may already have written their
+ * part of y.  Faults inside a kernel surface, as with any HIP kernel, at the
+ * caller's next synchronization.  The C ABI sees pointers, not buffer
+ * lengths: the caller guarantees that each buffer holds the shape given by
+ * (M, N, K, bits, group_size) and its dtype (the Python binding checks the
+ * tensor shapes before calling).
  */
 #ifndef QMV_H
 #define QMV_H
@@ -120,13 +127,18 @@ int qmv_affine_ex(const uint32_t* w_packed, const void* scales, const void* bias
 /* Resources and launch shape of the kernel the library would use for a call
  * with these arguments (its first launch, when the call is cut into several
  * tiles of vectors; no launch is made; needs a gfx950 device for the
- * occupancy query).  Fields: vgprs (architected VGPRs per lane as compiled),
+ * occupancy query).  The arguments are those of qmv_affine_ex without the
+ * pointers and the stream, validated the same way; y_dt selects no instance
+ * (the output dtype is a run-time flag of every kernel) and is validated
+ * only.  Fields: vgprs (architected VGPRs per lane as compiled),
  * scratch_bytes (private memory per lane; 0 = no register spills), lds_bytes
  * per workgroup (dynamic), wg_size (threads), grid (workgroups),
- * waves_per_simd (resident waves per SIMD at this LDS/VGPR use), rows_per_wave,
- * k_windows (K windows the activation tile is staged in; 1 = whole K),
- * prefetch_units (units of R rows x one 64-lane step whose loads each
- * wavefront keeps in flight). */
+ * waves_per_simd (wavefronts per SIMD on the busiest compute unit: its
+ * resident workgroups times their wavefronts over its four SIMDs),
+ * rows_per_wave, k_windows (K windows the activation tile is staged in;
+ * 1 = whole K), prefetch_units (units of R rows x one 64-lane step whose
+ * loads each wavefront keeps in flight).  The HIP runtime's function
+ * attributes report no scalar register count, so there is no sgprs field. */
 typedef struct {
     int vgprs;
     int scratch_bytes;
@@ -140,11 +152,12 @@ typedef struct {
 } qmv_kernel_info_t;
 
 int qmv_kernel_info(int M, int N, int K, int bits, int group_size, qmv_dtype x_dt,
-                    int rows_per_wave, qmv_kernel_info_t* out);
+                    qmv_dtype sb_dt, qmv_dtype y_dt, int rows_per_wave,
+                    qmv_kernel_info_t* out);
 
 /* Measurement aid, not part of the product: reads `bytes` bytes at `buf` (device
- * memory, 16-byte aligned, bytes a positive multiple of 16) with the one-vector
- * qmv's launch shape and 128-bit non-temporal loads.  Its time is the
+ * memory, 16-byte aligned, bytes a positive multiple of 16) with four
+ * 8-wavefront workgroups per compute unit and 128-bit non-temporal loads.  Its time is the
  * streaming-read ceiling a one-launch kernel of that shape reaches on that many
  * bytes, against which the qmv's fraction of the HBM peak is read.  With
  * `checksum` nonzero it also XORs the XOR of all 32-bit words of the buffer into
@@ -154,6 +167,16 @@ int qmv_kernel_info(int M, int N, int K, int bits, int group_size, qmv_dtype x_d
  * launch, no other work.  Returns QMV_E_NULL, QMV_E_SHAPE, QMV_E_ALIGN or
  * QMV_E_LAUNCH on bad arguments or a refused launch. */
 int qmv_stream_read(const void* buf, long long bytes, uint32_t* out, int checksum, void* stream);
+
+/* The same measurement aid with its launch shape as arguments, for sweeping
+ * the ceiling: wg_per_cu workgroups per compute unit (1..32), waves_per_wg
+ * wavefronts per workgroup (1..16), batch loads in flight per lane (1, 2, 4,
+ * 8 or 16), and interleave = 0 (each wavefront reads its own contiguous span
+ * of 1 KiB runs) or 1 (instruction j of wavefront w reads run j*TW + w, TW the
+ * wavefronts in the grid).  qmv_stream_read is (4, 8, 4, 0).  Other values
+ * return QMV_E_SHAPE. */
+int qmv_stream_read_ex(const void* buf, long long bytes, uint32_t* out, int checksum,
+                       int wg_per_cu, int waves_per_wg, int batch, int interleave, void* stream);
 
 /*
  * mxfp4 mode: y = qmv(x) with FP4 (E2M1) codes and one E8M0 scale per block of

@@ -74,6 +74,10 @@ class Oracle:
         L.orc_e2m1_to_f64.restype = ctypes.c_double
         L.orc_e8m0_to_f64.argtypes = [ctypes.c_uint]
         L.orc_e8m0_to_f64.restype = ctypes.c_double
+        L.orc_qmv_affine_mag.argtypes = [P, P, I, P, I, P, I, I, I, I, I, I]
+        L.orc_qmv_affine_mag.restype = I
+        L.orc_qmv_mxfp4_mag.argtypes = [P, P, I, P, I, I, I, I]
+        L.orc_qmv_mxfp4_mag.restype = I
         self.L = L
 
     def qmv(self, w_packed, scales, biases, x, *, bits, group_size, sb_dtype, x_dtype,
@@ -116,6 +120,37 @@ class Oracle:
         if rc != 0:
             raise ValueError(f"oracle rejected the request (code {rc})")
         return out
+
+    def qmv_mag(self, scales, biases, x, *, bits, group_size, sb_dtype, x_dtype,
+                nthreads: int = 0) -> np.ndarray:
+        """mag[M][N] (float64): the sum of the magnitudes of each output's terms,
+        sum_g (2^(bits+2)|scale| + |bias|) * sum_{k in g} |x[m][k]|, for the
+        a-priori bound |y - y_ref| <= gamma_d * mag of an fp32 evaluation."""
+        scales = np.ascontiguousarray(scales, dtype=np.uint16)
+        biases = np.ascontiguousarray(biases, dtype=np.uint16)
+        x = np.ascontiguousarray(x, dtype=np.float32 if x_dtype == F32 else np.uint16)
+        N = scales.shape[0]
+        M, K = x.shape
+        assert scales.shape[1] * group_size == K and biases.shape == scales.shape
+        mag = np.zeros((M, N), dtype=np.float64)
+        rc = self.L.orc_qmv_affine_mag(_ptr(scales), _ptr(biases), sb_dtype, _ptr(x), x_dtype,
+                                       _ptr(mag), M, N, K, bits, group_size, nthreads)
+        if rc != 0:
+            raise ValueError(f"oracle rejected the shape (code {rc})")
+        return mag
+
+    def qmv_mxfp4_mag(self, scales, x, *, x_dtype, nthreads: int = 0) -> np.ndarray:
+        """mag[M][N] (float64) of the mxfp4 mode: sum_b 2^(E-127) * 6 * sum_{k in b} |x[m][k]|."""
+        scales = np.ascontiguousarray(scales, dtype=np.uint8)
+        x = np.ascontiguousarray(x, dtype=np.float32 if x_dtype == F32 else np.uint16)
+        N = scales.shape[0]
+        M, K = x.shape
+        assert scales.shape[1] * 32 == K
+        mag = np.zeros((M, N), dtype=np.float64)
+        rc = self.L.orc_qmv_mxfp4_mag(_ptr(scales), _ptr(x), x_dtype, _ptr(mag), M, N, K, nthreads)
+        if rc != 0:
+            raise ValueError(f"oracle rejected the shape (code {rc})")
+        return mag
 
     def qmv_mxfp4(self, w_packed, scales, x, *, x_dtype, nthreads: int = 0) -> np.ndarray:
         """y_ref[M][N] (float64) of the mxfp4 mode.

@@ -177,6 +177,56 @@ int orc_qmv_affine_at(const uint32_t* w, const void* scales, const void* biases,
     return 0;
 }
 
+/*
+ * Term magnitude of each output, for an a-priori bound on the rounding error
+ * of any fp32 evaluation of the grouped form:
+ *
+ *   mag[m][n] = sum_g ( 2^(bits+2) |scale[n][g]| + |bias[n][g]| ) * sum_{k in g} |x[m][k]|
+ *
+ * Every code satisfies 0 <= q < 2^bits.  An evaluation may add an offset
+ * 0 <= c <= 2^bits to every code and remove it again as -c*scale*sum(x) (equal
+ * in real arithmetic, as the grouped and dequantized forms are: mlxcel issue
+ * "an order-preserving streamed qmv would give MTP the fast kernel and
+ * byte-identity together", section "Correction to the obvious sketch"); its
+ * terms scale*(q + c)*x, -c*scale*x and bias*x then have magnitudes summing to
+ * at most (3*2^bits |scale| + |bias|)|x| < (2^(bits+2) |scale| + |bias|)|x|.
+ * A sum evaluated in fp32 through at most d roundings per
+ * term differs from the exact sum by at most gamma_d = d*u/(1 - d*u) (u = 2^-24)
+ * times the sum of the magnitudes of its terms (the standard bound for
+ * floating-point summation), so |y - y_ref| <= gamma_d * mag.  The bound holds
+ * whatever the value of y, including outputs that cancel far below their
+ * terms.  The codes do not enter it, so w is not an argument.
+ */
+int orc_qmv_affine_mag(const void* scales, const void* biases, int sb_dt, const void* x,
+                       int x_dt, double* mag, int M, int N, int K, int bits, int gs,
+                       int nthreads)
+{
+    int rc = check(M, N, K, bits, gs);
+    if (rc) return rc;
+    const int G = K / gs;
+    const double span = ldexp(1.0, bits + 2);
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+    #pragma omp parallel for schedule(static)
+    for (int n = 0; n < N; ++n)
+        for (int m = 0; m < M; ++m) {
+            double acc = 0.0;
+            for (int g = 0; g < G; ++g) {
+                double A = 0.0;
+                for (int k = g * gs; k < (g + 1) * gs; ++k)
+                    A += fabs(elem(x, (size_t)m * (size_t)K + (size_t)k, x_dt));
+                double s = fabs(elem(scales, (size_t)n * G + g, sb_dt));
+                double b = fabs(elem(biases, (size_t)n * G + g, sb_dt));
+                acc += (span * s + b) * A;
+            }
+            mag[(size_t)m * N + n] = acc;
+        }
+    return 0;
+}
+
 /* ------------------------------------------------------------------ mxfp4
  * Microscaling FP4 (the "mxfp4" quantization mode the MLX pages list beside
  * the affine one; the pages do not define it, so the definition is the OCP
@@ -237,6 +287,38 @@ int orc_qmv_mxfp4(const uint32_t* w, const uint8_t* scales, const void* x, int x
     for (int n = 0; n < N; ++n)
         for (int m = 0; m < M; ++m)
             y[(size_t)m * N + n] = one_mx(w, scales, x, x_dt, m, n, K);
+    return 0;
+}
+
+/*
+ * Term magnitude of each mxfp4 output, for the same kind of a-priori bound:
+ *   mag[m][n] = sum_b X[n][b] * 6 * sum_{k in b} |x[m][k]|
+ * (6 is the largest E2M1 magnitude, so X*6 bounds |X * e2m1(q)|).  A block
+ * scale of NaN (E = 255) gives NaN.
+ */
+int orc_qmv_mxfp4_mag(const uint8_t* scales, const void* x, int x_dt, double* mag,
+                      int M, int N, int K, int nthreads)
+{
+    if (M < 0 || N < 0 || K < 0) return -3;
+    if (K % 32) return -4;
+    const int B = K / 32;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+    #pragma omp parallel for schedule(static)
+    for (int n = 0; n < N; ++n)
+        for (int m = 0; m < M; ++m) {
+            double acc = 0.0;
+            for (int b = 0; b < B; ++b) {
+                double A = 0.0;
+                for (int k = b * 32; k < (b + 1) * 32; ++k)
+                    A += fabs(elem(x, (size_t)m * (size_t)K + (size_t)k, x_dt));
+                acc += orc_e8m0_to_f64(scales[(size_t)n * B + b]) * 6.0 * A;
+            }
+            mag[(size_t)m * N + n] = acc;
+        }
     return 0;
 }
 

@@ -300,6 +300,59 @@ def pin_sampled_matches_full(orc):
     assert np.array_equal(z, y[ms, ns])
 
 
+def pin_magnitude(orc):
+    """The term magnitude of the a-priori error bound.  Closed form on x = +-e_k:
+    mag[k][n] = 2^(bits+2)|scale[n][g(k)]| + |bias[n][g(k)]| exactly (the signs
+    of x, scales and biases must not matter); mag(2x) = 2 mag(x) exactly; and
+    mag dominates every output's terms: mag >= |x| @ |W|^T with W = scale*q + bias
+    dequantized densely by numpy (so it also dominates |y|)."""
+    for (N, K, bits, gs, sb, xdt) in SHAPES:
+        p = gen.make_problem(N=N, K=K, bits=bits, gs=gs, sb=sb, x_dtype=xdt, seed=313 + K)
+        G = K // gs
+        sdt, xdc = (F16 if sb == "f16" else BF16), (F32 if xdt == "f32" else BF16)
+        s64 = sb_to_f64(p.scales, sb)
+        flip = (np.arange(N * G).reshape(N, G) % 3) == 0
+        sc = f64_to_bits(np.where(flip, -s64, s64), sb)          # some negative scales
+        sv, bv = sb_to_f64(sc, sb), sb_to_f64(p.biases, sb)
+        ks = np.arange(0, K, max(1, K // 24))
+        e = np.zeros((ks.size, K), dtype=np.float64)
+        e[np.arange(ks.size), ks] = np.where(np.arange(ks.size) % 2 == 0, 1.0, -1.0)
+        xe = e.astype(np.float32) if xdt == "f32" else f64_to_bits(e, "bf16")
+        mag = orc.qmv_mag(sc, p.biases, xe, bits=bits, group_size=gs, sb_dtype=sdt, x_dtype=xdc)
+        want = (2.0 ** (bits + 2)) * np.abs(sv[:, ks // gs]).T + np.abs(bv[:, ks // gs]).T
+        assert np.array_equal(mag, want), (N, K, bits, gs)
+        xv = x_to_f64(p.x[:4], xdt)
+        m1 = orc.qmv_mag(sc, p.biases, p.x[:4], bits=bits, group_size=gs, sb_dtype=sdt, x_dtype=xdc)
+        x2 = (p.x[:4] * np.float32(2.0)).astype(np.float32) if xdt == "f32" else f64_to_bits(2.0 * xv, "bf16")
+        m2 = orc.qmv_mag(sc, p.biases, x2, bits=bits, group_size=gs, sb_dtype=sdt, x_dtype=xdc)
+        assert np.array_equal(m2, 2.0 * m1)
+        q = decode_unpackbits(p.w_packed, bits).astype(np.float64)
+        W = np.repeat(sv, gs, axis=1) * q + np.repeat(bv, gs, axis=1)
+        assert np.all(m1 >= np.abs(xv) @ np.abs(W).T * (1 - 1e-12)), (N, K, bits, gs)
+
+
+def pin_round_outputs(orc):
+    """fp64 -> fp32 -> bf16 rounding of the outputs.  fp64 values off the fp32
+    grid, and exact fp32 midpoints (ties), round to nearest even: the expected
+    fp32 is picked by comparing distances in exact fp64 arithmetic, the tie by
+    the even significand; the bf16 step then matches torch on that fp32."""
+    rng = np.random.default_rng(21)
+    base = (rng.standard_normal(4000) * np.exp2(rng.integers(-60, 60, 4000))).astype(np.float32)
+    lo = base.astype(np.float64)
+    hi = np.nextafter(base, np.float32(np.inf)).astype(np.float64)
+    frac = rng.random(4000)
+    frac[:1000] = 0.5                                            # exact midpoints
+    v = lo + (hi - lo) * frac                                    # exact in fp64 for a midpoint
+    mid = lo + (hi - lo) * 0.5
+    even_lo = (base.view(np.uint32) & np.uint32(1)) == 0
+    pick_lo = (v < mid) | ((v == mid) & even_lo)
+    want32 = np.where(pick_lo, base, np.nextafter(base, np.float32(np.inf))).astype(np.float32)
+    got32, got16 = orc.round_outputs(v)
+    assert np.array_equal(got32.view(np.uint32), want32.view(np.uint32))
+    want16 = torch.from_numpy(want32.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got16, want16)
+
+
 # ------------------------------------------------------------- mxfp4 mode ---
 
 def _mx_golden():
@@ -352,7 +405,30 @@ def pin_mx_readout(orc):
         assert np.array_equal(y, mult * table[p.q[:, ks].T]), E
 
 
+def pin_mx_magnitude(orc):
+    """The mxfp4 term magnitude: on x = +-e_k it is 6 * 2^(E-127) exactly; a row
+    with a NaN scale (E = 255) in any block is NaN for every vector (NaN * 0 is
+    NaN, as in the product itself); mag(2x) = 2 mag(x), and it dominates
+    |x| @ |W|^T for the dense dequantized weights."""
+    p = gen.make_mx_problem(6, 128, "f32", 8, e_lo=0, e_hi=254)
+    sc = p.scales.copy()
+    sc[2, 1] = 255
+    ks = np.array([0, 5, 31, 32, 70, 127])
+    x = np.zeros((ks.size, 128), dtype=np.float32)
+    x[np.arange(ks.size), ks] = np.where(np.arange(ks.size) % 2 == 0, 1.0, -1.0)
+    mag = orc.qmv_mxfp4_mag(sc, x, x_dtype=F32)
+    want = 6.0 * np.ldexp(1.0, sc[:, ks // 32].astype(np.int64) - 127).T
+    want[:, 2] = np.nan
+    assert np.array_equal(mag, want, equal_nan=True)
+    p = gen.make_mx_problem(9, 256, "bf16", 9, e_lo=100, e_hi=140)
+    xv = x_to_f64(p.x[:3], "bf16")
+    m1 = orc.qmv_mxfp4_mag(p.scales, p.x[:3], x_dtype=BF16)
+    m2 = orc.qmv_mxfp4_mag(p.scales, f64_to_bits(2.0 * xv, "bf16"), x_dtype=BF16)
+    assert np.array_equal(m2, 2.0 * m1)
+    assert np.all(m1 >= np.abs(xv) @ np.abs(_mx_dense(p)).T * (1 - 1e-12))
+
+
 ALL_PINS = [pin_codec_golden, pin_2bit_float_floor_exhaustive, pin_4bit_nibbles_exhaustive,
             pin_readout, pin_worked_examples, pin_bruteforce_dequant, pin_closed_forms,
-            pin_conversions, pin_sampled_matches_full,
-            pin_mx_codes_golden, pin_mx_bruteforce, pin_mx_readout]
+            pin_conversions, pin_sampled_matches_full, pin_magnitude, pin_round_outputs,
+            pin_mx_codes_golden, pin_mx_bruteforce, pin_mx_readout, pin_mx_magnitude]

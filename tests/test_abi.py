@@ -27,7 +27,7 @@ def L():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == ["qmv_affine", "qmv_affine_ex", "qmv_kernel_info", "qmv_mxfp4",
-                                    "qmv_status_string", "qmv_stream_read"]
+                                    "qmv_status_string", "qmv_stream_read", "qmv_stream_read_ex"]
 
 
 def test_exports_every_declared_symbol(L):
@@ -81,9 +81,75 @@ def test_rejects_bad_arguments(L, kw, code):
 def test_kernel_info_validates(L):
     from bit_quantized_gemv_amd import qmv
     info = qmv.KernelInfo()
-    assert L.qmv_kernel_info(1, 256, 512, 3, 64, 2, 0, ctypes.byref(info)) == 2
-    assert L.qmv_kernel_info(65537, 256, 512, 4, 64, 2, 0, ctypes.byref(info)) == 5
-    assert L.qmv_kernel_info(1, 256, 512, 4, 64, 2, 0, None) == 1
+    # (M, N, K, bits, gs, x_dt, sb_dt, y_dt, R, out)
+    assert L.qmv_kernel_info(1, 256, 512, 3, 64, 2, 2, 2, 0, ctypes.byref(info)) == 2
+    assert L.qmv_kernel_info(65537, 256, 512, 4, 64, 2, 2, 2, 0, ctypes.byref(info)) == 5
+    assert L.qmv_kernel_info(1, 256, 512, 4, 64, 2, 2, 2, 0, None) == 1
+    assert L.qmv_kernel_info(1, 256, 512, 4, 64, 2, 0, 2, 0, ctypes.byref(info)) == 7   # sb_dt f32
+    assert L.qmv_kernel_info(1, 256, 512, 4, 64, 2, 2, 1, 0, ctypes.byref(info)) == 7   # y_dt f16
+    assert L.qmv_kernel_info(1, 256, 512, 4, 64, 2, 2, 2, 5, ctypes.byref(info)) == 8
+
+
+def _tensors(N=4, K=512, bits=4, gs=64, M=1):
+    import torch
+    w = torch.zeros(N, K * bits // 32, dtype=torch.int32)
+    s = torch.zeros(N, K // gs, dtype=torch.bfloat16)
+    x = torch.zeros(M, K, dtype=torch.bfloat16)
+    return w, s, s.clone(), x
+
+
+@pytest.mark.parametrize("what", ["w_cols", "w_rows", "scales", "biases", "bits", "gs", "K",
+                                  "dtype_mix", "x_3d"])
+def test_binding_checks_shapes_before_the_call(what):
+    """Wrong shapes raise in the binding, before anything reaches the C ABI
+    (which sees only pointers): the checks run before the device check, so
+    CPU tensors show it."""
+    import torch
+    from bit_quantized_gemv_amd import qmv
+    w, s, b, x = _tensors()
+    kw = dict(bits=4, group_size=64)
+    if what == "w_cols":
+        w = w[:, :-4].contiguous()
+    elif what == "w_rows":        # scales and biases for 5 rows, w for 4
+        s, b = torch.zeros(5, 8, dtype=torch.bfloat16), torch.zeros(5, 8, dtype=torch.bfloat16)
+    elif what == "scales":
+        s = torch.zeros(4, 4, dtype=torch.bfloat16)
+    elif what == "biases":
+        b = torch.zeros(4, 16, dtype=torch.bfloat16)
+    elif what == "bits":
+        kw["bits"] = 2            # w holds 4-bit rows: K would be 1024, x says 512
+    elif what == "gs":
+        kw["group_size"] = 128    # scales hold 8 groups, 128 would need 4
+    elif what == "K":
+        x = torch.zeros(1, 480, dtype=torch.bfloat16)
+    elif what == "dtype_mix":
+        b = b.half()
+    elif what == "x_3d":
+        x = x.view(1, 1, 512)
+    err = TypeError if what == "dtype_mix" else ValueError
+    with pytest.raises(err) as ei:
+        qmv.affine(w, s, b, x, **kw)
+    assert "CUDA" not in str(ei.value), str(ei.value)
+
+
+@pytest.mark.parametrize("what", ["w_cols", "scales_rows", "scales_cols", "K"])
+def test_mxfp4_binding_checks_shapes_before_the_call(what):
+    import torch
+    from bit_quantized_gemv_amd import qmv
+    w = torch.zeros(4, 64, dtype=torch.int32)
+    s = torch.zeros(4, 16, dtype=torch.uint8)
+    x = torch.zeros(1, 512, dtype=torch.bfloat16)
+    if what == "w_cols":
+        w = torch.zeros(4, 60, dtype=torch.int32)
+    elif what == "scales_rows":
+        s = torch.zeros(3, 16, dtype=torch.uint8)
+    elif what == "scales_cols":
+        s = torch.zeros(4, 15, dtype=torch.uint8)
+    elif what == "K":
+        x = torch.zeros(1, 500, dtype=torch.bfloat16)
+    with pytest.raises(ValueError) as ei:
+        qmv.mxfp4(w, s, x)
+    assert "CUDA" not in str(ei.value), str(ei.value)
 
 
 def test_binding_refuses_cpu_tensors():
@@ -106,6 +172,12 @@ def test_stream_read_validates(L):
     assert L.qmv_stream_read(4096, 0, 8192, 0, None) == 4
     assert L.qmv_stream_read(4104, 1024, 8192, 0, None) == 6          # QMV_E_ALIGN
     assert L.qmv_stream_read(4096, 1024, 8194, 0, None) == 6
+    I = ctypes.c_int
+    L.qmv_stream_read_ex.argtypes = [P, ctypes.c_longlong, P, I, I, I, I, I, P]
+    for shape in ((0, 8, 4, 0), (33, 8, 4, 0), (4, 0, 4, 0), (4, 17, 4, 0), (4, 8, 3, 0),
+                  (4, 8, 32, 0), (4, 8, 4, 2)):
+        assert L.qmv_stream_read_ex(4096, 1024, 8192, 0, *shape, None) == 4, shape
+    assert L.qmv_stream_read_ex(None, 1024, 8192, 0, 4, 8, 4, 0, None) == 1
 
 
 def test_mxfp4_validates(L):

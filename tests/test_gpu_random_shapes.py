@@ -1,9 +1,10 @@
-"""GPU parity on a seeded sweep of random shapes and dtypes: ragged N, K from
-one group up, both code widths and group sizes, every activation / parameter
-/ output dtype, M up to 27 (several tiles of vectors) and forced rows per
-wavefront.  Each case is checked against the oracle, the bf16 output against
-the rounded fp32 output, and its first and last vector against one-vector
-calls bit for bit."""
+"""GPU parity on a seeded sweep of random shapes and dtypes: ragged N (one to
+three rows included), K from one group up, both code widths and group sizes,
+every activation / parameter / output dtype, M up to 27 (several tiles of
+vectors) and forced rows per wavefront.  Each case is checked against the
+oracle (normwise and under the a-priori rounding bound), the bf16 output
+against the rounded fp32 output, and its first and last vector against
+one-vector calls bit for bit."""
 import numpy as np
 import pytest
 import torch
@@ -14,23 +15,25 @@ from inputs import gen
 pytestmark = pytest.mark.gpu
 
 
-def _cases(n=160, seed=2024):
+def _cases(n=160, seed=2024, n_hi=321, seed0=3000):
     rng = np.random.default_rng(seed)
     out = []
     for i in range(n):
         bits = int(rng.choice([2, 4]))
         gs = int(rng.choice([64, 128]))
         K = gs * int(rng.integers(1, 81))
-        N = int(rng.integers(1, 321))
+        N = int(rng.integers(1, n_hi))
         sb = str(rng.choice(["f16", "bf16"]))
         xdt = str(rng.choice(["f32", "bf16"]))
         M = int(rng.choice([1, 2, 3, 4, 5, 7, 9, 13, 14, 20, 27]))
         R = int(rng.choice([0, 0, 1, 2, 3, 4]))
-        out.append((N, K, bits, gs, sb, xdt, M, R, 3000 + i))
+        out.append((N, K, bits, gs, sb, xdt, M, R, seed0 + i))
     return out
 
 
-@pytest.mark.parametrize("case", _cases(),
+# 160 shapes with up to 320 rows, and 40 with one to three rows (vectors whose
+# few outputs may cancel: held to the a-priori bound where they miss 2e-5)
+@pytest.mark.parametrize("case", _cases() + _cases(40, 2025, 4, 3500),
                          ids=lambda c: f"N{c[0]}_K{c[1]}_b{c[2]}_g{c[3]}_{c[4]}_{c[5]}_M{c[6]}_R{c[7]}")
 def test_random_shape_vs_oracle(case):
     N, K, bits, gs, sb, xdt, M, R, seed = case
@@ -40,7 +43,8 @@ def test_random_shape_vs_oracle(case):
     xd = U.x_to_dev(xs, xdt)
     U.say(f"random N={N} K={K} bits={bits} gs={gs} sb={sb} x={xdt} M={M} R={R}")
     y = U.gpu(p, dev, M, torch.float32, R=R, x=xd)
-    U.check_parity(y, U.ref(p, M, x=xs), f"N={N} K={K} M={M}")
+    U.check_parity(y, U.ref(p, M, x=xs), f"N={N} K={K} M={M}", mag=U.affine_mag(p, M, x=xs),
+                   depth=U.affine_depth(K, bits, gs, xdt))
     y16 = U.gpu(p, dev, M, torch.bfloat16, R=R, x=xd)
     assert torch.equal(y16.view(torch.int16), U.rne_bf16(y).view(torch.int16))
     for m in sorted({0, M - 1}):

@@ -27,7 +27,17 @@ MUTANTS = {
     "f16_subnormal_flushed": ("v = ldexp((double)f, -24);", "v = 0.0;"),
     "bf16_ties_away": ("(lower == 0x8000u && (upper & 1u))", "(lower == 0x8000u)"),
     "row_stride_wrong": ("(size_t)n * (size_t)(K * bits / 32)", "(size_t)n * (size_t)(K * bits / 32 - 1)"),
+    # term magnitude of the a-priori error bound
+    "mag_bias_dropped": ("acc += (span * s + b) * A;", "acc += (span * s) * A;"),
+    "mag_span_short": ("ldexp(1.0, bits + 2);", "ldexp(1.0, bits + 1);"),
+    "mag_x_signed": ("A += fabs(elem(x, (size_t)m * (size_t)K + (size_t)k, x_dt));\n                double s",
+                     "A += elem(x, (size_t)m * (size_t)K + (size_t)k, x_dt);\n                double s"),
+    "mag_bias_signed": ("double b = fabs(elem(biases,", "double b = (elem(biases,"),
+    # output rounding
+    "round_f32_truncates": ("float f = (float)y[i];", "float f = (float)y[i]; { uint32_t t; memcpy(&t, &f, 4); "
+                            "if (fabs((double)f) > fabs(y[i])) { t -= 1u; memcpy(&f, &t, 4); } }"),
     # mxfp4 mode
+    "mx_mag_six": ("* 6.0 * A;", "* 4.0 * A;"),
     "e2m1_exponent_bias": ("ldexp(1.0 + 0.5 * m, e - 1)", "ldexp(1.0 + 0.5 * m, e)"),
     "e2m1_subnormal": ("(e == 0) ? 0.5 * m :", "(e == 0) ? 1.0 * m :"),
     "e2m1_sign_ignored": ("ldexp(1.0 + 0.5 * m, e - 1);\n    return sign ? -v : v;",
