@@ -84,22 +84,37 @@ struct Plan {
     int R, W, PF, lds, grid, blocks_per_cu;
 };
 
-// LDS layout and K windows.  Returns QMV_E_SHAPE if one wave step of
-// activations for all M vectors does not fit in LDS.
-int make_plan(int M, int N, int K, int bits, int gs, bool xf32, bool sbf, int R, int W, int PF, Plan& pl)
+// LDS layout and K windows for workgroups of W wavefronts that walk up to
+// `per` row blocks each.  Returns QMV_E_SHAPE if one wave step of activations
+// for all M vectors does not fit in LDS.
+int make_plan(int M, int N, int K, int bits, int gs, bool xf32, bool sbf, int R, int W, int PF, int per,
+              Plan& pl)
 {
     const int G = K / gs;
     const int chunks = K * bits / 128;
     const int nsteps = (chunks + qmv::kWave - 1) / qmv::kWave;
     const int xcb = (128 / bits) * (xf32 ? 4 : 2);
+    // Whole K, scale/bias copies in LDS (the instances without K windows):
+    // each of a wavefront's `per` row blocks takes a slot of whole 16-byte
+    // pieces from the piece that holds its rows' first byte, and the slots
+    // of all of them must fit one wave-wide load (kMetaBytes); the copies sit
+    // in a static array of kMaxWaves * 2 * kMetaBytes bytes, and the lane
+    // offsets of the loads are 32-bit.
+    const long long m_slot = 16 * ((14 + 2LL * R * G + 15) / 16);
+    const long long sb_bytes = (long long)N * G * 2;
+    const int lpg = gs * bits / 128;
+    const bool own_rows = (lpg == 2 || lpg == 4) && R % lpg == 0;   // instances that hold copies
+    const bool copies_fit = per * m_slot <= qmv::kMetaBytes && sb_bytes <= (1LL << 31) - 16;
+    const long long static_lds = (long long)qmv::kMaxWaves * 2 * qmv::kMetaBytes;
     // per vector and window: padded activations and a float2 per chunk
     // (dot-chain start, group sum)
-    int ws = nsteps, x_m = 0, sc_bytes = 0, total = 0;
+    int ws = nsteps, x_m = 0, sc_bytes = 0;
+    long long total = 0;
     for (;;) {
         const int logical = ws * qmv::kWave * xcb;
         x_m = logical + logical / 16;
         sc_bytes = M * ws * qmv::kWave * 8;
-        total = M * x_m + sc_bytes;
+        total = (long long)M * x_m + sc_bytes;
         if (total <= qmv::kLdsBytes || ws == 1) break;
         --ws;
     }
@@ -124,10 +139,16 @@ int make_plan(int M, int N, int K, int bits, int gs, bool xf32, bool sbf, int R,
     p.x_m_bytes = x_m;
     p.s_off = M * x_m;
     pl.lds = p.s_off + sc_bytes;
+    // Whole K: instances whose lanes fold their own rows hold the copies when
+    // they fit (beside the static array); where they do not, the K-windowed
+    // instance, which loads the scales and biases per unit, serves one window.
+    const bool mlds = nwin == 1 && own_rows && copies_fit && pl.lds + static_lds <= qmv::kLdsBytes;
+    p.m_slot = mlds ? (int)m_slot : 0;
+    p.sb_last = mlds ? (int)((sb_bytes - 1) & ~15LL) : 0;
     pl.R = R;
     pl.W = W;
     pl.PF = PF;
-    pl.fn = pick_kernel(bits, gs, xf32, sbf, R, PF, M, nwin > 1);
+    pl.fn = pick_kernel(bits, gs, xf32, sbf, R, PF, M, nwin > 1 || (own_rows && !mlds));
     return QMV_OK;
 }
 
@@ -197,24 +218,37 @@ bool occupancy(KernelFn kfn, int W, int lds, int dev, int& blocks, int& scratch)
 int try_plan(int M, int N, int K, int bits, int gs, bool xf32, bool sbf, int R, int W, int PF,
              int dev, int cus, Plan& pl, bool& shape_ok)
 {
-    if (make_plan(M, N, K, bits, gs, xf32, sbf, R, W, PF, pl) != QMV_OK) return 0;
-    shape_ok = true;
-    if (pl.fn == nullptr) return 0;
-    int nb = 0, scratch = 0;
-    if (!occupancy(pl.fn, W, pl.lds, dev, nb, scratch)) return -1;
-    if (nb == 0) return 0;
-    const int n_rb = pl.p.n_rb;
-    const int cap = nb * cus;
-    int per = (n_rb + cap - 1) / cap;         // row blocks per workgroup
-    // Memory-bound calls: at least two row blocks per workgroup while that still
-    // leaves a workgroup for every compute unit -- the activations are staged
-    // once for both and the second block's loads overlap the first's compute
-    // (measured: 1% on 15360 x 3840 at 4 bits, and the choice the occupancy
-    // already makes at 2 bits, where a row is one wave step).
-    if (M <= 2 && per == 1 && n_rb >= 2 * cus) per = 2;
-    pl.grid = (n_rb + per - 1) / per;
-    pl.blocks_per_cu = nb;
-    return 1;
+    // Whether a whole-K plan holds the scale/bias copies of its row blocks
+    // depends on the row blocks per workgroup, which follow from the resident
+    // workgroups, which the instance and its LDS decide: start from one block
+    // and plan again until the plan holds every block its workgroups walk.
+    int reserve = 1;
+    for (int iter = 0; iter < 16; ++iter) {
+        if (make_plan(M, N, K, bits, gs, xf32, sbf, R, W, PF, reserve, pl) != QMV_OK) return 0;
+        shape_ok = true;
+        if (pl.fn == nullptr) return 0;
+        int nb = 0, scratch = 0;
+        if (!occupancy(pl.fn, W, pl.lds, dev, nb, scratch)) return -1;
+        if (nb == 0) return 0;
+        const int n_rb = pl.p.n_rb;
+        const int cap = nb * cus;
+        int per = (n_rb + cap - 1) / cap;         // row blocks per workgroup
+        // Memory-bound calls: at least two row blocks per workgroup while that
+        // still leaves a workgroup for every compute unit -- the activations
+        // are staged once for both and the second block's loads overlap the
+        // first's compute (measured: 1% on 15360 x 3840 at 4 bits, and the
+        // choice the occupancy already makes at 2 bits, where a row is one
+        // wave step).
+        if (M <= 2 && per == 1 && n_rb >= 2 * cus) per = 2;
+        if (pl.p.m_slot > 0 && per > reserve) {
+            reserve = per;
+            continue;
+        }
+        pl.grid = (n_rb + per - 1) / per;
+        pl.blocks_per_cu = nb;
+        return 1;
+    }
+    return 0;
 }
 
 // Rows the busiest compute unit processes: workgroups are dealt out whole, so
@@ -312,7 +346,7 @@ int vectors_per_launch(int M, int N, int K, int bits, int gs, bool xf32)
     int cap = 0;
     for (int mc = std::min(M, QMV_TILE_M); mc >= 1; --mc) {
         Plan pl;
-        if (make_plan(mc, N, K, bits, gs, xf32, true, 1, 1, 1, pl) == QMV_OK) {
+        if (make_plan(mc, N, K, bits, gs, xf32, true, 1, 1, 1, 1, pl) == QMV_OK) {
             cap = mc;
             break;
         }
@@ -337,7 +371,7 @@ int tile_vectors(int M, int N, int K, int bits, int gs, bool xf32, bool sbf, int
     if (pl.p.nwin == 1 || pl.p.n_rb <= pl.grid) return mc;
     for (int mk = mc - 1; mk >= (mc + 1) / 2; --mk) {
         Plan q;
-        if (make_plan(mk, N, K, bits, gs, xf32, sbf, 1, 1, 1, q) == QMV_OK && q.p.nwin == 1) {
+        if (make_plan(mk, N, K, bits, gs, xf32, sbf, 1, 1, 1, 1, q) == QMV_OK && q.p.nwin == 1) {
             const int tiles = (M + mk - 1) / mk;
             return (M + tiles - 1) / tiles;
         }
@@ -420,7 +454,7 @@ int qmv_kernel_info(int M, int N, int K, int bits, int group_size, qmv_dtype x_d
     if (hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(pl.fn)) != hipSuccess) return QMV_E_LAUNCH;
     out->vgprs = attr.numRegs;
     out->scratch_bytes = (int)attr.localSizeBytes;
-    out->lds_bytes = pl.lds;
+    out->lds_bytes = pl.lds + (int)attr.sharedSizeBytes;
     out->wg_size = pl.W * qmv::kWave;
     out->grid = pl.grid;
     // workgroups on the busiest compute unit (at most the resident count),
@@ -432,6 +466,7 @@ int qmv_kernel_info(int M, int N, int K, int bits, int group_size, qmv_dtype x_d
     out->rows_per_wave = pl.R;
     out->k_windows = pl.p.nwin;
     out->prefetch_units = pl.PF;
+    out->meta_lds = pl.p.m_slot > 0 ? 1 : 0;
     return QMV_OK;
 }
 

@@ -104,7 +104,16 @@ struct Params {
     int s_off;           // LDS offset of SC[M][win_steps * 64]: per chunk a float2 (dot-chain
                          // start -2^bits * chunk sum for bf16 activations, 0 for fp32;
                          // sum of the chunk's group)
+    int m_slot;          // whole-K instances: bytes of a row block's scale (bias) copy,
+                         // 16 * ceil((14 + 2 * R * G) / 16); at most kMetaBytes per wavefront
+                         // for all its row blocks
+    int sb_last;         // offset of the last 16-byte piece of the scale (bias) tensor
 };
+
+// Whole-K instances: LDS bytes per wavefront for its copy of the scales (and
+// as many for the biases) of all its row blocks -- one 16-byte piece per lane
+// of one wave-wide load.
+constexpr int kMetaBytes = 1024;
 
 // ------------------------------------------------------------------ helpers
 
@@ -256,6 +265,18 @@ __device__ __forceinline__ float f16_to_f32_here(unsigned short h)
     float f;
     asm volatile("v_cvt_f32_f16 %0, %1" : "=v"(f) : "v"(h));
     return f;
+}
+
+// v as a scalar register.  A value derived from scalars only is uniform, but
+// after divergent control flow the compiler may keep it in a vector register
+// (dropping a readfirstlane as redundant), and a buffer resource built from a
+// vector register costs a waterfall loop around every load that uses it.  The
+// "s" constraints make it materialize the value in an SGPR.
+__device__ __forceinline__ int in_sgpr(int v)
+{
+    int r;
+    asm("s_mov_b32 %0, %1" : "=s"(r) : "s"(v));
+    return r;
 }
 
 // Hides how an offset was computed, so the compiler keeps one unconditional
@@ -578,7 +599,10 @@ constexpr int waves_hint(int BITS, bool XF32, int R, int M, int PF, bool WIN)
 }
 
 // WIN: the instance restages the activations per K window (when x[0..M)[0..K)
-// does not fit in LDS); instances without it require p.nwin == 1.
+// does not fit in LDS) and loads each unit's scales and biases with its
+// weights; it also serves one window where the scale/bias copies of the
+// instances without it do not fit.  Instances without it require p.nwin == 1
+// and p.m_slot > 0.
 template <int BITS, int GS, int R, int M, int PF, bool XF32, bool SBF, bool WIN>
 __global__ __launch_bounds__(kMaxWaves * kWave) __attribute__((amdgpu_waves_per_eu(waves_hint(BITS, XF32, R, M, PF, WIN))))
 void qmv_affine_kernel(const Params p)
@@ -603,6 +627,14 @@ void qmv_affine_kernel(const Params p)
     // it loads only those rows' values (the rows lpg*k + l % lpg).
     constexpr bool OWNLOAD = (LPG == 2 || LPG == 4) && (R % LPG == 0);
     constexpr int RL = OWNLOAD ? R / LPG : R;
+    // Whole-K instances whose lanes each fold their own rows (OWNLOAD) read
+    // each group's scale and bias from LDS: with the weight prologue every
+    // wavefront loads the scale and bias rows of all its row blocks (two
+    // wave-wide loads), and its first unit stores them in a static LDS array,
+    // so the unit loop issues weight loads only.  The other instances --
+    // and the K-windowed one, also used for whole K where the copies would
+    // not fit -- load the values of each unit with its weights.
+    constexpr bool MLDS = !WIN && OWNLOAD;
     constexpr int SKIP = GROUPED ? (LPG == 4 ? 2 : 1) : 0;   // reduction levels inside a group
     constexpr int V = RS * M;
     constexpr int P = pow2_at_least(V);
@@ -640,8 +672,8 @@ void qmv_affine_kernel(const Params p)
         // every input of the resources is wave-uniform; readfirstlane makes that
         // explicit (a resource the compiler cannot prove uniform costs a
         // waterfall loop around every load)
-        const int rbase = __builtin_amdgcn_readfirstlane(min(i_row0, p.N - 1));
-        const int records = __builtin_amdgcn_readfirstlane((is_rb < n_my) ? -1 : 0);
+        const int rbase = in_sgpr(__builtin_amdgcn_readfirstlane(min(i_row0, p.N - 1)));
+        const int records = in_sgpr(__builtin_amdgcn_readfirstlane((is_rb < n_my) ? -1 : 0));
         i_wr = make_rsrc(reinterpret_cast<const uint8_t*>(p.w) + (size_t)rbase * p.row_bytes, records);
         i_sr = make_rsrc(p.s + (size_t)rbase * p.G, records);
         i_br = make_rsrc(p.b + (size_t)rbase * p.G, records);
@@ -667,7 +699,7 @@ void qmv_affine_kernel(const Params p)
 #pragma unroll
         for (int r = 0; r < R; ++r) wv[r] = buf_load_nt(i_wr, wo, i_sw[r]);
 #pragma unroll
-        for (int k = 0; k < RL; ++k) {
+        for (int k = 0; k < (MLDS ? 0 : RL); ++k) {
             if constexpr (OWNLOAD) {
                 sv[k] = buf_load_u16(i_sr, mo + i_ps[k], 0);
                 bv[k] = buf_load_u16(i_br, mo + i_ps[k], 0);
@@ -689,6 +721,35 @@ void qmv_affine_kernel(const Params p)
         }
     };
 
+    // Whole K: one wave-wide 128-bit load fetches the scales of all row
+    // blocks of this wavefront (another the biases), issued with the weight
+    // prologue; the first unit, which waits for the prologue's weights anyway,
+    // stores them in this wavefront's part of a static LDS array, where every
+    // unit reads them.  Lane l takes piece l % SP of block l / SP, SP =
+    // m_slot / 16 pieces per block: block b's rows [r0, r0 + nr) (a block past
+    // N reads row N-1) are the bytes from r0*G*2, taken from the 16-byte piece
+    // that holds their first byte, so they start (r0*G*2) % 16 bytes into the
+    // block's slot.  Lanes past the last block, and pieces past the tensor's
+    // last piece, read that last piece again.  The tensors start 16-byte
+    // aligned, so every piece holds tensor bytes and lies in their page.
+    uint8_t* mcopy = nullptr;
+    uint4 mpiece_s = make_uint4(0, 0, 0, 0), mpiece_b = make_uint4(0, 0, 0, 0);
+    if constexpr (MLDS) {
+        __shared__ __align__(16) uint8_t meta_lds[kMaxWaves][2][kMetaBytes];
+        mcopy = &meta_lds[wave][0][0];
+    }
+    auto load_meta = [&]() {
+        const int sp = p.m_slot >> 4;
+        const int b = lane / sp;
+        const int pc = lane - b * sp;
+        const int bb = min(b, n_my - 1);
+        const int r0 = min((((int)blockIdx.x + bb * grid) * W + wave) * R, p.N - 1);
+        const int start = (int)(((uint32_t)r0 * (uint32_t)(p.G * 2)) & ~15u);
+        const int off = min(start + pc * 16, p.sb_last);
+        mpiece_s = buf_load(make_rsrc(p.s, -1), off);
+        mpiece_b = buf_load(make_rsrc(p.b, -1), off);
+    };
+
     const uint32_t magic = opaque_u32(code_magic<BITS>());
     Stager<BITS, GS, M, XF32> stg;
     uint4 wb[NS][R];
@@ -697,8 +758,12 @@ void qmv_affine_kernel(const Params p)
 #pragma unroll
         for (int s = 0; s < PF; ++s) issue(wb[s], sb[s], bb[s]);
     };
-    // activation loads first, then the weight prologue, then the conversion
-    stg.stage(p, xr, lds, 0, prologue);
+    // activation loads first, then (whole K) the scale/bias pieces, then the
+    // weight prologue, then the conversion
+    stg.stage(p, xr, lds, 0, [&]() {
+        if constexpr (MLDS) load_meta();
+        prologue();
+    });
     __syncthreads();
 
     float acc[RS][M];
@@ -707,6 +772,22 @@ void qmv_affine_kernel(const Params p)
 #pragma unroll
         for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
     int c_rb = 0, c_t = 0, c_tw = 0, c_win = 0;   // unit consumed next; its step within the window
+    // Whole K: byte offsets of the lane's scale in the LDS copies.  Per row
+    // block: the block's slot, the rows' start in it, and row k of the lane
+    // (rows past N read row N-1); per unit the lane's group, clamped to the
+    // row's last group.
+    int m_roff[RL];
+    const int m_goff = (lane / LPG) * 2, m_gmax = (p.G - 1) * 2;
+    auto meta_block = [&](int rb) {
+        if constexpr (MLDS) {
+            const int r0 = min((((int)blockIdx.x + rb * grid) * W + wave) * R, p.N - 1);
+            const int nr1 = min(R, p.N - r0) - 1;
+            const int base = rb * p.m_slot + (int)(((uint32_t)r0 * (uint32_t)(p.G * 2)) & 15u);
+#pragma unroll
+            for (int k = 0; k < RL; ++k) m_roff[k] = base + min(k * LPG + lane % LPG, nr1) * p.G * 2;
+        }
+    };
+    meta_block(0);
     const int xl = lds_phys(lane * XCB);          // LDS offset of the lane's chunk in a window's first step
     for (int ub = 0; ub < n_units; ub += NS) {
 #pragma unroll
@@ -721,8 +802,10 @@ void qmv_affine_kernel(const Params p)
                         c_tw = 0;
                         ++c_win;
                     }
-                    if (c_tw == 0 && (c_rb > 0 || t > 0)) {
-                        // K windows: restage this window (the first one was staged above)
+                    if (p.nwin > 1 && c_tw == 0 && (c_rb > 0 || t > 0)) {
+                        // K windows: restage this window (the first one was staged
+                        // above; with one window, used for whole K where the
+                        // scale/bias copies do not fit, it stays)
                         __syncthreads();
                         stg.stage(p, xr, lds, c_win, [] {});
                         __syncthreads();
@@ -741,26 +824,56 @@ void qmv_affine_kernel(const Params p)
                 const int rb0 = (((int)blockIdx.x + c_rb * grid) * W + wave) * R;   // block's first row
                 float sv[RS], bv[RS];
                 float fs[RL], fb[RL];
+                auto own_select = [&]() {
 #pragma unroll
-                for (int k = 0; k < RL; ++k) {
-                    fs[k] = SBF ? bf16_to_f32_here(sb[s][k]) : f16_to_f32_here(sb[s][k]);
-                    fb[k] = SBF ? bf16_to_f32_here(bb[s][k]) : f16_to_f32_here(bb[s][k]);
-                }
-#pragma unroll
-                for (int k = 0; k < RS; ++k) {
-                    if constexpr (GROUPED) {
-                        sv[k] = fs[k];
-                        bv[k] = fb[k];
-                    } else if constexpr (OWNLOAD) {
-                        const bool own = (lane % LPG) == (k % LPG);
-                        sv[k] = own ? fs[k / LPG] : 0.0f;
-                        bv[k] = own ? fb[k / LPG] : 0.0f;
-                    } else {
-                        const bool own = (lane % LPG) == ((rb0 + k) % LPG);
-                        sv[k] = own ? fs[k] : 0.0f;
-                        bv[k] = own ? fb[k] : 0.0f;
+                    for (int k = 0; k < RS; ++k) {
+                        if constexpr (GROUPED) {
+                            sv[k] = fs[k];
+                            bv[k] = fb[k];
+                        } else if constexpr (OWNLOAD) {
+                            const bool own = (lane % LPG) == (k % LPG);
+                            sv[k] = own ? fs[k / LPG] : 0.0f;
+                            bv[k] = own ? fb[k / LPG] : 0.0f;
+                        } else {
+                            const bool own = (lane % LPG) == ((rb0 + k) % LPG);
+                            sv[k] = own ? fs[k] : 0.0f;
+                            bv[k] = own ? fb[k] : 0.0f;
+                        }
                     }
+                };
+                if constexpr (!MLDS) {
+#pragma unroll
+                    for (int k = 0; k < RL; ++k) {
+                        fs[k] = SBF ? bf16_to_f32_here(sb[s][k]) : f16_to_f32_here(sb[s][k]);
+                        fb[k] = SBF ? bf16_to_f32_here(bb[s][k]) : f16_to_f32_here(bb[s][k]);
+                    }
+                    own_select();
                 }
+                // Whole K: the scale and bias of this unit come from the LDS
+                // copies (stored there by the first unit); each path calls this
+                // once its activation reads are issued, so no wait for the copies
+                // sits in front of those reads.
+                auto finish_meta = [&]() {
+                    if constexpr (MLDS) {
+                        if (ub == 0 && s == 0) {
+                            // (the store waits for the pieces: keep the activation
+                            // reads issued above ahead of it)
+                            __builtin_amdgcn_sched_barrier(0);
+                            *reinterpret_cast<uint4*>(mcopy + lane * 16) = mpiece_s;
+                            *reinterpret_cast<uint4*>(mcopy + kMetaBytes + lane * 16) = mpiece_b;
+                        }
+                        const int gofs = min(t * (kWave / LPG) * 2 + m_goff, m_gmax);
+#pragma unroll
+                        for (int k = 0; k < RL; ++k) {
+                            const uint8_t* e = mcopy + m_roff[k] + gofs;
+                            const uint32_t hs = *reinterpret_cast<const unsigned short*>(e);
+                            const uint32_t hb = *reinterpret_cast<const unsigned short*>(e + kMetaBytes);
+                            fs[k] = SBF ? __uint_as_float(hs << 16) : f16_bits_to_f32(hs);
+                            fb[k] = SBF ? __uint_as_float(hb << 16) : f16_bits_to_f32(hb);
+                        }
+                        own_select();
+                    }
+                };
                 const int xo0 = xl + c_tw * XSTEP;            // chunk's LDS offset (never straddles padding)
                 const int cl = c_tw * kWave + lane;           // chunk within the window
 
@@ -846,6 +959,7 @@ void qmv_affine_kernel(const Params p)
                         float S[M], c0[M];
 #pragma unroll
                         for (int m = 0; m < M; ++m) read_x(m, xo0, xp[m], S[m], c0[m]);
+                        finish_meta();
                         if constexpr (GROUPED) {
 #pragma unroll
                             for (int k = 0; k < RS; ++k) {
@@ -925,6 +1039,7 @@ void qmv_affine_kernel(const Params p)
                             for (int r = 1; r < R; ++r) c0[r] = *cs;
                         };
                         read_xr(0, xo0, xq[0], Sq[0], cq[0]);
+                        finish_meta();
                         uint32_t qp[R][NP];
                         if constexpr (GROUPED) {
 #pragma unroll
@@ -989,6 +1104,7 @@ void qmv_affine_kernel(const Params p)
                         }
                     };
                     read_x(0, xo0, xq[0]);
+                    finish_meta();
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         float qv[R][VPW];
@@ -1054,6 +1170,7 @@ void qmv_affine_kernel(const Params p)
                     c_tw = 0;
                     c_win = 0;
                     ++c_rb;
+                    meta_block(c_rb);
                 } else {
                     ++c_t;
                     ++c_tw;

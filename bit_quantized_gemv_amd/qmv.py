@@ -26,7 +26,7 @@ class QmvError(RuntimeError):
 class KernelInfo(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in ("vgprs", "scratch_bytes", "lds_bytes", "wg_size",
                                              "grid", "waves_per_simd", "rows_per_wave",
-                                             "k_windows", "prefetch_units")]
+                                             "k_windows", "prefetch_units", "meta_lds")]
 
 
 _lib = None

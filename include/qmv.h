@@ -132,12 +132,14 @@ int qmv_affine_ex(const uint32_t* w_packed, const void* scales, const void* bias
  * (the output dtype is a run-time flag of every kernel) and is validated
  * only.  Fields: vgprs (architected VGPRs per lane as compiled),
  * scratch_bytes (private memory per lane; 0 = no register spills), lds_bytes
- * per workgroup (dynamic), wg_size (threads), grid (workgroups),
+ * per workgroup (dynamic plus static), wg_size (threads), grid (workgroups),
  * waves_per_simd (wavefronts per SIMD on the busiest compute unit: its
  * resident workgroups times their wavefronts over its four SIMDs),
  * rows_per_wave, k_windows (K windows the activation tile is staged in;
  * 1 = whole K), prefetch_units (units of R rows x one 64-lane step whose
- * loads each wavefront keeps in flight).  The HIP runtime's function
+ * loads each wavefront keeps in flight), meta_lds (1: each wavefront loads
+ * the scales and biases of all its rows once and reads them from LDS; 0: it
+ * loads each unit's with the unit's weights).  The HIP runtime's function
  * attributes report no scalar register count, so there is no sgprs field. */
 typedef struct {
     int vgprs;
@@ -149,6 +151,7 @@ typedef struct {
     int rows_per_wave;
     int k_windows;
     int prefetch_units;
+    int meta_lds;
 } qmv_kernel_info_t;
 
 int qmv_kernel_info(int M, int N, int K, int bits, int group_size, qmv_dtype x_dt,
