@@ -850,26 +850,38 @@ void qmv_affine_kernel(const Params p)
                     own_select();
                 }
                 // Whole K: the scale and bias of this unit come from the LDS
-                // copies (stored there by the first unit); each path calls this
-                // once its activation reads are issued, so no wait for the copies
-                // sits in front of those reads.
+                // copies, read ahead of the activations.  The first unit stores
+                // the copies after its activation reads (the store waits for the
+                // pieces) and reads them again there.  Each path calls
+                // finish_meta() once its activation reads are issued; the
+                // conversion there waits for the copies' reads only.
+                uint32_t hs[RL], hb[RL];
+                const bool first_unit = (ub == 0 && s == 0);
+                auto meta_read = [&]() {
+                    const int gofs = min(t * (kWave / LPG) * 2 + m_goff, m_gmax);
+#pragma unroll
+                    for (int k = 0; k < RL; ++k) {
+                        const uint8_t* e = mcopy + m_roff[k] + gofs;
+                        hs[k] = *reinterpret_cast<const unsigned short*>(e);
+                        hb[k] = *reinterpret_cast<const unsigned short*>(e + kMetaBytes);
+                    }
+                };
+                if constexpr (MLDS) meta_read();   // (first unit: read again after its store)
                 auto finish_meta = [&]() {
                     if constexpr (MLDS) {
-                        if (ub == 0 && s == 0) {
-                            // (the store waits for the pieces: keep the activation
-                            // reads issued above ahead of it)
+                        if (first_unit) {
                             __builtin_amdgcn_sched_barrier(0);
                             *reinterpret_cast<uint4*>(mcopy + lane * 16) = mpiece_s;
                             *reinterpret_cast<uint4*>(mcopy + kMetaBytes + lane * 16) = mpiece_b;
+                            meta_read();
                         }
-                        const int gofs = min(t * (kWave / LPG) * 2 + m_goff, m_gmax);
 #pragma unroll
                         for (int k = 0; k < RL; ++k) {
-                            const uint8_t* e = mcopy + m_roff[k] + gofs;
-                            const uint32_t hs = *reinterpret_cast<const unsigned short*>(e);
-                            const uint32_t hb = *reinterpret_cast<const unsigned short*>(e + kMetaBytes);
-                            fs[k] = SBF ? __uint_as_float(hs << 16) : f16_bits_to_f32(hs);
-                            fb[k] = SBF ? __uint_as_float(hb << 16) : f16_bits_to_f32(hb);
+                            // (volatile: the conversion stays here, after the
+                            // activation reads, instead of next to the reads)
+                            const unsigned short s16 = (unsigned short)hs[k], b16 = (unsigned short)hb[k];
+                            fs[k] = SBF ? bf16_to_f32_here(s16) : f16_to_f32_here(s16);
+                            fb[k] = SBF ? bf16_to_f32_here(b16) : f16_to_f32_here(b16);
                         }
                         own_select();
                     }
