@@ -12,7 +12,8 @@ one copy of the inputs.  Inputs rotate over enough copies (>= 1 GiB) that the
 timing starts.  Before the first measurement the process runs untimed calls
 for at least 30 ms of GPU time (clocks settle), then each measurement runs its
 W warm-up calls and times graphs of K and of 2K calls on the launch stream
-between HIP events (median of 9 alternating replays each): the per-call time
+between HIP events (medians of alternating replays, at least 9 of each and
+at least 20 ms of GPU time per graph size): the per-call time
 is (T(2K) - T(K)) / K, the time of K whole calls without the fixed cost of a
 graph replay.
 
@@ -125,17 +126,24 @@ def settle_clocks(launch, ncopies, torch, min_ms=SETTLE_MS):
     return calls, done_ms
 
 
-def time_calls(launch, ncopies, M, steps, warmup, torch, replays=9):
+REPLAY_MS = 20.0            # GPU time each graph size is replayed for, at least
+MIN_REPLAYS = 9
+
+
+def time_calls(launch, ncopies, M, steps, warmup, torch, replays=None):
     """Per-call microseconds of `steps` calls, with the fixed cost of a graph
     replay cancelled.
 
     `warmup` untimed calls first; then two HIP graphs are captured on the
     launch stream, one of K = steps calls and one of 2K calls (inputs rotating
-    over the copies), and replayed alternately `replays` times between HIP
-    events on that stream.  A replay costs its kernels plus a fixed launch
-    overhead (about 20 us here), so the difference of the median replay times,
-    T(2K) - T(K), is the time of K whole calls with that overhead removed; the
-    per-call time is that difference over K.  Returns (us per call, details)."""
+    over the copies), and replayed alternately between HIP events on that
+    stream -- `replays` times, or by default at least MIN_REPLAYS times and
+    until each size has run for REPLAY_MS (short graphs are replayed more
+    often: their median is noisier).  A replay costs its kernels plus a fixed
+    launch overhead (about 20 us here), so the difference of the median replay
+    times, T(2K) - T(K), is the time of K whole calls with that overhead
+    removed; the per-call time is that difference over K.  Returns (us per
+    call, details)."""
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
         for i in range(warmup):
@@ -155,7 +163,9 @@ def time_calls(launch, ncopies, M, steps, warmup, torch, replays=9):
         g.replay()
     stream.synchronize()
     t1, t2 = [], []
-    for _ in range(replays):
+    i = 0
+    while (i < replays) if replays is not None else (i < MIN_REPLAYS or sum(t1) < REPLAY_MS):
+        i += 1
         for g, ts in ((g1, t1), (g2, t2)):
             start = torch.cuda.Event(enable_timing=True)
             end = torch.cuda.Event(enable_timing=True)
@@ -168,7 +178,7 @@ def time_calls(launch, ncopies, M, steps, warmup, torch, replays=9):
     m1 = sorted(t1)[len(t1) // 2]
     m2 = sorted(t2)[len(t2) // 2]
     us = (m2 - m1) * 1000.0 / steps
-    return us, {"graph_K_ms": round(m1, 4), "graph_2K_ms": round(m2, 4),
+    return us, {"graph_K_ms": round(m1, 4), "graph_2K_ms": round(m2, 4), "replays": len(t1),
                 "us_per_call_graph_K": round(m1 * 1000.0 / steps, 3)}
 
 
@@ -512,8 +522,9 @@ def main():
     r1, r13 = results[1], results[Mmax]
     flops13 = 2 * Mmax * N * K
     timing = (f"per call = (T(2K) - T(K)) / K: HIP graphs of K = {args.steps} and {2 * args.steps} calls "
-              f"(inputs rotating over {ncopies} copies) replayed alternately 9 times each between HIP "
-              f"events on the launch stream, medians; {args.warmup} untimed calls before each "
+              f"(inputs rotating over {ncopies} copies) replayed alternately {r1['det']['replays']} times each "
+              f"(at least 9, and 20 ms of GPU time per size) between HIP events on the launch stream, "
+              f"medians; {args.warmup} untimed calls before each "
               f"measurement, and {settle_calls} untimed calls ({settle_ms:.0f} ms of GPU time) before "
               f"the first")
     out = {
