@@ -446,8 +446,8 @@ struct Stager {
     // unconditionally (so the compiler counts the loads in flight exactly);
     // `between` runs next (the caller issues its weight prologue there, so the
     // activation requests are ahead of the weight stream); then those rounds
-    // are converted and stored.  Rounds past XB (long windows only) are
-    // loaded and stored one at a time afterwards.
+    // are converted and stored.  Rounds past XB (long windows, many vectors)
+    // follow in batches of XB, each batch's loads issued together.
     template <class F>
     __device__ void stage(const Params& p, __amdgpu_buffer_rsrc_t xr, uint8_t* lds, int win, F&& between)
     {
@@ -475,11 +475,27 @@ struct Stager {
                 }
             }
         }
-        for (int i = XB; i < rounds; ++i) {
-            const int m = i / rpm, j = i - (i / rpm) * rpm;
-            uint4 d[NLD];
-            load(p, xr, m, j, d);
-            store(p, lds, m, j, d);
+        for (int base = XB; base < rounds; base += XB) {
+            uint4 d[XB][NLD];
+            int m = base / rpm, j = base - (base / rpm) * rpm;
+#pragma unroll
+            for (int i = 0; i < XB; ++i) {
+                load(p, xr, m, j, d[i]);
+                if (++j == rpm) {
+                    j = 0;
+                    ++m;
+                }
+            }
+            m = base / rpm;
+            j = base - (base / rpm) * rpm;
+#pragma unroll
+            for (int i = 0; i < XB; ++i) {
+                if (base + i < rounds) store(p, lds, m, j, d[i]);
+                if (++j == rpm) {
+                    j = 0;
+                    ++m;
+                }
+            }
         }
         zero_tail(p, lds);
     }
