@@ -16,8 +16,8 @@
 //   * A wavefront owns R consecutive rows (row blocking): in a step it loads the
 //     chunk of each of its rows and reads the activations of that chunk from
 //     LDS once for all R rows.  A (row block, step) pair is a unit.  Each
-//     wavefront keeps the weights, scales and biases of the next PF units in
-//     flight in a register ring; the loads of a unit are issued before the
+//     wavefront keeps the weights (and, where loaded per unit, the scales and
+//     biases) of the next PF units in flight in a register ring; the loads of a unit are issued before the
 //     compute of the unit PF places earlier, and a scheduling barrier keeps
 //     the compiler from sinking them below it.
 //   * A workgroup of W wavefronts stages the activations x[0..M)[K-window] in
@@ -26,12 +26,18 @@
 //     in one round).
 //     All activation loads are issued before the first weight load, and the
 //     weight prologue is in flight while the activations are converted.
-//   * Each lane loads the scale and bias of its own group, of the rows whose
+//   * Each lane uses the scale and bias of its own group, of the rows whose
 //     group it owns (step 4 below) when the rows per wavefront are a multiple
 //     of lpg, else of every row (zeroing them in registers where it does not
-//     own the group).  Rows past N and chunks past a row's end read clamped,
-//     in-bounds addresses; the activations, chain starts and group sums of
-//     chunks past the row's end are zero in LDS, so those lanes add nothing.
+//     own the group).  Whole-K instances with a multiple of lpg rows per
+//     wavefront fetch the scale and bias rows of all the wavefront's row
+//     blocks once (two wave-wide 128-bit loads) into LDS and read them there;
+//     the others load each unit's values with its weights.  Rows past N and
+//     chunks past a row's end read clamped, in-bounds addresses; the
+//     activations, chain starts and group sums of chunks past the row's end
+//     are zero in LDS, so those lanes add nothing.
+//   * Activation staging issues the loads of a batch of rounds together; long
+//     windows and many vectors take several batches.
 //   * The weight decode of a chunk happens once per step, outside the loop over
 //     the M vectors; every vector then reuses the decoded registers.
 //
