@@ -389,6 +389,123 @@ def sweep_ceiling(args, q, gen, torch, np, dev):
     print(json.dumps({"sweep": "stream_ceiling_best", **best}), flush=True)
 
 
+def _pcts(v, np):
+    """p10, p50, p90 and max of a sequence."""
+    v = np.asarray(v, dtype=np.float64)
+    return [float(np.percentile(v, 10)), float(np.percentile(v, 50)), float(np.percentile(v, 90)),
+            float(v.max())]
+
+
+def _timeline_stats(bufs, clock_khz, np):
+    """Per-sample statistics of stamped launches (ns after the sample's earliest
+    wavefront start), then the median over the samples."""
+    ns_per_tick = 1e6 / clock_khz
+    rows = []
+    for b in bufs:
+        a = b.cpu().numpy()
+        t = (a[:, :3] - a[:, 0].min()).astype(np.float64) * ns_per_tick
+        ids = a[:, 3]
+        cu = (ids >> 32) * 256 + ((ids >> 8) & 0xFF)   # XCC, then HW_ID bits 8..15
+        keys, inv, counts = np.unique(cu, return_inverse=True, return_counts=True)
+        cu_end = np.full(len(keys), -np.inf)
+        np.maximum.at(cu_end, inv, t[:, 2])
+        rows.append({"start": _pcts(t[:, 0], np), "staged": _pcts(t[:, 1], np),
+                     "end": _pcts(t[:, 2], np), "staging": _pcts(t[:, 1] - t[:, 0], np),
+                     "after_staging": _pcts(t[:, 2] - t[:, 1], np), "cu_end": _pcts(cu_end, np),
+                     "cus": len(keys), "waves_per_cu": [int(counts.min()), int(counts.max())]})
+
+    def med(key):
+        return [round(float(np.median([r[key][i] for r in rows])), 0) for i in range(4)]
+    return {"ns_p10_p50_p90_max": {k: med(k) for k in ("start", "staged", "end", "staging",
+                                                       "after_staging", "cu_end")},
+            "cus": int(np.median([r["cus"] for r in rows])),
+            "waves_per_cu": [int(np.median([r["waves_per_cu"][0] for r in rows])),
+                             int(np.median([r["waves_per_cu"][1] for r in rows]))]}
+
+
+def timeline(args, q, gen, torch, np, dev):
+    """Per-wavefront timeline of the library's launch, from the stamped
+    instance of the same kernel (qmv_affine_timeline): the 4-bit group-64
+    projection shapes at M = 1 and 13.  Each sample is one stamped call on a
+    rotating copy, enqueued right after a few product calls on other copies
+    (so the GPU is busy and the copy cold in the caches, as in the timed
+    bench); per sample the stamps are taken relative to its earliest wavefront
+    start, and the figures below are medians over the samples:
+    p10 / p50 / p90 / max over the wavefronts of each event (start,
+    activations staged, end; ns), of the staging time (staged - start) and of
+    the time after staging (end - staged), and of the compute units' last
+    wavefront end; the compute units used and the wavefronts per compute unit
+    (min, max).  The product's and the stamped instance's us per call (bench
+    timing) are printed beside them.  `x_hot` repeats the product timing and
+    the stamps with every call reading one activation buffer (weights,
+    scales and biases still rotate), as when x was just written by the
+    previous operation: the difference is the cost of cold activations.  A
+    call the library cuts into tiles of vectors (17408 x 5120 at 13 vectors)
+    is stamped on its first tile's vectors.  One JSON line per point."""
+    samples = max(5, min(args.steps, 50))
+    settled = False
+    for name in ("up_4b_15360x3840", "down_4b_3840x15360", "up_4b_17408x5120", "down_4b_5120x17408"):
+        p = gen.make_problem(name)
+        N, K, bits, gs = p.N, p.K, p.bits, p.gs
+        nc = max(2, -(-ROTATE_BYTES // alg_bytes(N, K, bits, gs, 13)))
+        copies, ptrs = device_problem(p, torch, np, dev, nc)
+        hot = [(w, s, b, ptrs[0][3], y) for (w, s, b, x, y) in ptrs]
+        if not settled:
+            settle_clocks(affine_launcher(q, p, ptrs), nc, torch)
+            settled = True
+        for M in (1, 13):
+            # a call cut into tiles of vectors is stamped on its first tile
+            info = q.TimelineInfo()
+            while True:
+                st = q.timeline_ptr(*ptrs[0][:5], M, N, K, q.DT_BF16, 0, None, 0, info)
+                if st != 5 or M == 1:
+                    break
+                M -= 1
+            if st != 0:
+                raise q.QmvError(st, "qmv_affine_timeline")
+            bufs = [torch.zeros((info.waves, q.STAMPS), dtype=torch.int64, device=dev)
+                    for _ in range(samples)]
+
+            def stamped_launcher(pp):
+                def launch_stamped(i, M, stream, buf=None):
+                    b = bufs[0] if buf is None else buf
+                    st = q.timeline_ptr(*pp[i][:5], M, N, K, q.DT_BF16, 0, b.data_ptr(), b.numel(),
+                                        info, stream.cuda_stream)
+                    if st != 0:
+                        raise q.QmvError(st, "qmv_affine_timeline")
+                return launch_stamped
+
+            def run(pp):
+                launch, launch_stamped = affine_launcher(q, p, pp), stamped_launcher(pp)
+                us, _ = time_calls(launch, nc, M, args.steps, args.warmup, torch)
+                us_st, _ = time_calls(launch_stamped, nc, M, args.steps, args.warmup, torch)
+                stream = torch.cuda.current_stream()
+                c = 0
+                for j in range(samples):
+                    for _ in range(4):
+                        launch(c % nc, M, stream)
+                        c += 1
+                    launch_stamped(c % nc, M, stream, bufs[j])
+                    c += 1
+                torch.cuda.synchronize()
+                return us, us_st, _timeline_stats(bufs, info.clock_khz, np)
+
+            us, us_st, cold = run(ptrs)
+            us_hot, _, warm = run(hot)
+            kinf = q.kernel_info(M, N, K, bits, gs)
+            print(json.dumps({
+                "timeline": name, "M": M, "rows_per_wave": kinf["rows_per_wave"], "grid": info.grid,
+                "waves": info.waves, "samples": samples,
+                "us_per_call": round(us, 3), "us_per_call_stamped": round(us_st, 3),
+                "vgprs": [info.product_vgprs, info.vgprs],
+                "blocks_per_cu": [info.product_blocks_per_cu, info.blocks_per_cu],
+                **cold,
+                "x_hot": {"us_per_call": round(us_hot, 3),
+                          "ns_p10_p50_p90_max": warm["ns_p10_p50_p90_max"]}}), flush=True)
+        del copies
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -409,6 +526,9 @@ def main():
                          "the 27B-class shapes, with resources and occupancy per point")
     ap.add_argument("--sweep-ceiling", action="store_true",
                     help="instead of the bench line, sweep the streaming-read ceiling's launch shape")
+    ap.add_argument("--timeline", action="store_true",
+                    help="instead of the bench line, per-wavefront timelines of the 4-bit projection "
+                         "shapes at M = 1 and 13 (stamped instance of the same kernel)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -431,6 +551,9 @@ def main():
         return
     if args.sweep_ceiling:
         sweep_ceiling(args, q, gen, torch, np, dev)
+        return
+    if args.timeline:
+        timeline(args, q, gen, torch, np, dev)
         return
     wl = gen.WORKLOADS[WORKLOAD]
     p = gen.make_problem(WORKLOAD)

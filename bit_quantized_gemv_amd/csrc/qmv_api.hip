@@ -31,6 +31,8 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb)
 
 int r_index(int R) { return R - 1; }   // R in 1..4
 
+static_assert(qmv::kStamps == QMV_STAMPS, "per-wavefront stamp record size");
+
 // Pure argument check (no HIP calls).
 int check_args(const uint32_t* w, const void* s, const void* b, const void* x, void* y, int M,
                int N, int K, int bits, int gs, int x_dt, int sb_dt, int y_dt, int R)
@@ -81,6 +83,7 @@ KernelFn pick_kernel(int bits, int gs, bool xf32, bool sbf, int R, int PF, int M
 struct Plan {
     Params p;
     KernelFn fn;
+    bool win;   // fn is a K-windowed instance
     int R, W, PF, lds, grid, blocks_per_cu;
 };
 
@@ -145,10 +148,24 @@ int make_plan(int M, int N, int K, int bits, int gs, bool xf32, bool sbf, int R,
     const bool mlds = nwin == 1 && own_rows && copies_fit && pl.lds + static_lds <= qmv::kLdsBytes;
     p.m_slot = mlds ? (int)m_slot : 0;
     p.sb_last = mlds ? (int)((sb_bytes - 1) & ~15LL) : 0;
+    p.m_div = mlds ? (8192 + (int)(m_slot / 16) - 1) / (int)(m_slot / 16) : 0;
+    // staging rounds per vector: 16-byte units (8 values; 16 for bf16
+    // activations with 2-bit codes) of a window over the workgroup's threads
+    {
+        const int uv = (!xf32 && bits == 2) ? 16 : 8;
+        const int vpc = 128 / bits;
+        const int nthr = W * qmv::kWave;
+        auto rounds_of = [&](int c_n) { return (c_n * vpc / uv + nthr - 1) / nthr; };
+        p.rpm_full = rounds_of(std::min(chunks, ws * qmv::kWave));
+        p.rpm_last = rounds_of(chunks - (nwin - 1) * ws * qmv::kWave);
+    }
+    p.rb_per = 0;    // set with the grid
+    p.rb_full = 0;
     pl.R = R;
     pl.W = W;
     pl.PF = PF;
-    pl.fn = pick_kernel(bits, gs, xf32, sbf, R, PF, M, nwin > 1 || (own_rows && !mlds));
+    pl.win = nwin > 1 || (own_rows && !mlds);
+    pl.fn = pick_kernel(bits, gs, xf32, sbf, R, PF, M, pl.win);
     return QMV_OK;
 }
 
@@ -190,9 +207,8 @@ int cu_count(int dev)
 
 // Resident workgroups per CU of an instance at a workgroup size and LDS size,
 // and its private bytes per lane.  False on a HIP error.
-bool occupancy(KernelFn kfn, int W, int lds, int dev, int& blocks, int& scratch)
+bool occupancy(const void* fn, int W, int lds, int dev, int& blocks, int& scratch)
 {
-    const void* fn = reinterpret_cast<const void*>(kfn);
     std::lock_guard<std::mutex> lk(g_mu);
     for (int i = 0; i < g_nocc; ++i)
         if (g_occ[i].fn == fn && g_occ[i].dev == dev && g_occ[i].lds == lds && g_occ[i].w == W) {
@@ -228,7 +244,7 @@ int try_plan(int M, int N, int K, int bits, int gs, bool xf32, bool sbf, int R, 
         shape_ok = true;
         if (pl.fn == nullptr) return 0;
         int nb = 0, scratch = 0;
-        if (!occupancy(pl.fn, W, pl.lds, dev, nb, scratch)) return -1;
+        if (!occupancy(reinterpret_cast<const void*>(pl.fn), W, pl.lds, dev, nb, scratch)) return -1;
         if (nb == 0) return 0;
         const int n_rb = pl.p.n_rb;
         const int cap = nb * cus;
@@ -246,6 +262,8 @@ int try_plan(int M, int N, int K, int bits, int gs, bool xf32, bool sbf, int R, 
         }
         pl.grid = (n_rb + per - 1) / per;
         pl.blocks_per_cu = nb;
+        pl.p.rb_per = (n_rb + pl.grid - 1) / pl.grid;
+        pl.p.rb_full = n_rb - (pl.p.rb_per - 1) * pl.grid;
         return 1;
     }
     return 0;
@@ -467,6 +485,66 @@ int qmv_kernel_info(int M, int N, int K, int bits, int group_size, qmv_dtype x_d
     out->k_windows = pl.p.nwin;
     out->prefetch_units = pl.PF;
     out->meta_lds = pl.p.m_slot > 0 ? 1 : 0;
+    return QMV_OK;
+}
+
+int qmv_affine_timeline(const uint32_t* w_packed, const void* scales, const void* biases,
+                        const void* x, void* y, int M, int N, int K, qmv_dtype y_dt,
+                        int rows_per_wave, uint64_t* stamps, long long stamps_len,
+                        qmv_timeline_info_t* info, void* stream)
+{
+    if (!info) return QMV_E_NULL;
+    int st = check_args(w_packed, scales, biases, x, y, M, N, K, 4, 64, QMV_DT_BF16, QMV_DT_BF16,
+                        y_dt, rows_per_wave);
+    if (st != QMV_OK) return st;
+    if (M > QMV_TILE_M) return QMV_E_M_RANGE;
+    if (stamps && !aligned(stamps, 8)) return QMV_E_ALIGN;
+    if (stamps && stamps_len < 1) return QMV_E_SHAPE;
+    if (stamps) {
+        const size_t nst = (size_t)stamps_len * 8;
+        const size_t nw = (size_t)N * (size_t)K / 2, nsb = (size_t)N * (size_t)(K / 64) * 2;
+        const size_t nx = (size_t)M * (size_t)K * 2, ny = (size_t)M * (size_t)N * dtype_bytes(y_dt);
+        if (overlap(stamps, nst, w_packed, nw) || overlap(stamps, nst, scales, nsb) ||
+            overlap(stamps, nst, biases, nsb) || overlap(stamps, nst, x, nx) || overlap(stamps, nst, y, ny))
+            return QMV_E_ALIAS;
+    }
+    // the call must be the one launch qmv_affine_ex would make
+    const int mc = tile_vectors(M, N, K, 4, 64, false, true, rows_per_wave);
+    if (mc < 1) return QMV_E_SHAPE;
+    if (mc < M) return QMV_E_M_RANGE;
+    Plan pl;
+    st = choose_plan(M, N, K, 4, 64, false, true, rows_per_wave, pl);
+    if (st != QMV_OK) return st;
+    const qmv::TimelineFn tfn = qmv::qmv_timeline_b4_g64_bf16[pl.win ? 1 : 0][pl.R - 1][M - 1];
+    int dev = 0, khz = 0, nb = 0, scratch = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return QMV_E_LAUNCH;
+    if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess) return QMV_E_LAUNCH;
+    if (!occupancy(reinterpret_cast<const void*>(tfn), pl.W, pl.lds, dev, nb, scratch)) return QMV_E_LAUNCH;
+    hipFuncAttributes ta, pa;
+    if (hipFuncGetAttributes(&ta, reinterpret_cast<const void*>(tfn)) != hipSuccess ||
+        hipFuncGetAttributes(&pa, reinterpret_cast<const void*>(pl.fn)) != hipSuccess)
+        return QMV_E_LAUNCH;
+    info->waves = pl.grid * pl.W;
+    info->wg_size = pl.W * qmv::kWave;
+    info->grid = pl.grid;
+    info->clock_khz = khz;
+    info->blocks_per_cu = nb;
+    info->product_blocks_per_cu = pl.blocks_per_cu;
+    info->vgprs = ta.numRegs;
+    info->product_vgprs = pa.numRegs;
+    if (!stamps) return QMV_OK;
+    if (stamps_len < (long long)info->waves * QMV_STAMPS) return QMV_E_SHAPE;
+    Params& p = pl.p;
+    p.w = w_packed;
+    p.s = static_cast<const uint16_t*>(scales);
+    p.b = static_cast<const uint16_t*>(biases);
+    p.x = static_cast<const uint8_t*>(x);
+    p.y = y;
+    p.y_bf16 = (y_dt == QMV_DT_BF16);
+    void* args[] = {&p, &stamps};
+    if (hipLaunchKernel(reinterpret_cast<const void*>(tfn), dim3(pl.grid), dim3(pl.W * qmv::kWave), args,
+                        (size_t)pl.lds, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return QMV_E_LAUNCH;
     return QMV_OK;
 }
 

@@ -40,6 +40,10 @@
 //     windows and many vectors take several batches.
 //   * The weight decode of a chunk happens once per step, outside the loop over
 //     the M vectors; every vector then reuses the decoded registers.
+//   * A measurement instance of the same kernel (one more argument) records,
+//     per wavefront, the real-time counter at its start, after staging and at
+//     its end, and where it ran; the product instances compile to the same
+//     code as without it.
 //
 // Per-row arithmetic (fixed by K, bits, group size and activation dtype; it
 // never depends on M, R, W, PF, the grid or the K-window size):
@@ -114,6 +118,11 @@ struct Params {
                          // 16 * ceil((14 + 2 * R * G) / 16); at most kMetaBytes per wavefront
                          // for all its row blocks
     int sb_last;         // offset of the last 16-byte piece of the scale (bias) tensor
+    int m_div;           // ceil(8192 / (m_slot / 16)): lane / (m_slot / 16) is (lane * m_div) >> 13
+    int rpm_full;        // staging rounds per vector of a full K window (of the whole K if one)
+    int rpm_last;        // ... of the last K window
+    int rb_per;          // row blocks of the workgroups that walk the most: ceil(n_rb / grid)
+    int rb_full;         // workgroups below this index walk rb_per blocks, the others rb_per - 1
 };
 
 // Whole-K instances: LDS bytes per wavefront for its copy of the scales (and
@@ -331,6 +340,7 @@ struct Stager {
     static constexpr int NLD = (XF32 || BITS == 2) ? 2 : 1;   // 16-byte loads per unit
     static constexpr int XB = ((M <= 2) ? 4 : (M <= 6 ? 8 : 16)) / NLD;  // rounds in flight
 
+    int nthr;     // threads in the workgroup
     int upm;      // units per vector in this window
     int rpm;      // rounds per vector
     int rounds;   // M * rpm
@@ -342,7 +352,7 @@ struct Stager {
         const int c_lo = win * p.win_steps * kWave;
         c_n = min(p.chunks - c_lo, p.win_steps * kWave);
         upm = c_n * VPC / UV;
-        rpm = (upm + (int)blockDim.x - 1) / (int)blockDim.x;
+        rpm = (win == p.nwin - 1) ? p.rpm_last : p.rpm_full;   // ceil(upm / threads)
         rounds = M * rpm;
         k_lo = c_lo * VPC;
     }
@@ -352,7 +362,7 @@ struct Stager {
     // unit; their data is not stored.
     __device__ void load(const Params& p, __amdgpu_buffer_rsrc_t xr, int m, int j, uint4 (&d)[NLD]) const
     {
-        const int l = j * (int)blockDim.x + (int)threadIdx.x;
+        const int l = j * nthr + (int)threadIdx.x;
         const int lc = min(l, upm - 1);
         const int mc = min(m, M - 1);
         const int off = (mc * p.K + k_lo + lc * UV) * (XF32 ? 4 : 2);
@@ -362,7 +372,7 @@ struct Stager {
 
     __device__ void store(const Params& p, uint8_t* lds, int m, int j, const uint4 (&d)[NLD]) const
     {
-        const int l = j * (int)blockDim.x + (int)threadIdx.x;
+        const int l = j * nthr + (int)threadIdx.x;
         const bool valid = l < upm;
         float2* SC = reinterpret_cast<float2*>(lds + p.s_off);
         uint8_t* dst = lds + m * p.x_m_bytes;
@@ -440,10 +450,10 @@ struct Stager {
         float2* SC = reinterpret_cast<float2*>(lds + p.s_off);
 #pragma unroll
         for (int m = 0; m < M; ++m) {
-            for (int j = (int)threadIdx.x; j < pieces; j += (int)blockDim.x)
+            for (int j = (int)threadIdx.x; j < pieces; j += nthr)
                 *reinterpret_cast<uint4*>(lds + m * p.x_m_bytes + lds_phys(c_n * XCB + 16 * j)) =
                     make_uint4(0, 0, 0, 0);
-            for (int j = (int)threadIdx.x; j < cw - c_n; j += (int)blockDim.x)
+            for (int j = (int)threadIdx.x; j < cw - c_n; j += nthr)
                 SC[m * cw + c_n + j] = make_float2(0.0f, 0.0f);
         }
     }
@@ -620,15 +630,46 @@ constexpr int waves_hint(int BITS, bool XF32, int R, int M, int PF, bool WIN)
     return (BITS == 4 && !XF32 && M == 1 && R <= 2 && PF == 1 && !WIN) ? 8 : 1;
 }
 
+// Per-wavefront record of the stamped (measurement) instances: the constant-
+// rate counter at the wavefront's start, once the activations are staged
+// (after the workgroup barrier) and at its end, and the hardware ids of where
+// it ran (XCC id in the high word, HW_ID in the low word).  Nothing is stamped
+// inside the unit loop: a stamp there changes the loop's code and register
+// use.
+constexpr int kStamps = 4;
+
+// Reads the constant-rate real-time counter and waits for it in the same asm
+// block, so no later wait on LDS reads waits on it.
+__device__ __forceinline__ uint64_t stamp_now()
+{
+    uint64_t t;
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_memrealtime %0\n\ts_waitcnt lgkmcnt(0)" : "=s"(t));
+    __builtin_amdgcn_sched_barrier(0);
+    return t;
+}
+
 // WIN: the instance restages the activations per K window (when x[0..M)[0..K)
 // does not fit in LDS) and loads each unit's scales and biases with its
 // weights; it also serves one window where the scale/bias copies of the
 // instances without it do not fit.  Instances without it require p.nwin == 1
 // and p.m_slot > 0.
-template <int BITS, int GS, int R, int M, int PF, bool XF32, bool SBF, bool WIN>
+// Stamps: the product instances take no further argument (Stamps empty).  The
+// measurement instance takes one, a uint64_t* to which lane 0 of each
+// wavefront writes its kStamps values at stamps[(workgroup * W + wave) *
+// kStamps ...] after its last unit; its code is the product's with the three
+// counter reads, two hardware-register reads and that store added.  (The stamps stay inside this one
+// definition: a kernel body moved into a device function compiles to
+// different code.)
+template <int BITS, int GS, int R, int M, int PF, bool XF32, bool SBF, bool WIN, class... Stamps>
 __global__ __launch_bounds__(kMaxWaves * kWave) __attribute__((amdgpu_waves_per_eu(waves_hint(BITS, XF32, R, M, PF, WIN))))
-void qmv_affine_kernel(const Params p)
+void qmv_affine_kernel(const Params p, Stamps... stamp_ptr)
 {
+    constexpr bool STAMP = sizeof...(Stamps) > 0;
+    static_assert(sizeof...(Stamps) == 0 || (sizeof...(Stamps) == 1 && (std::is_same_v<Stamps, uint64_t*> && ...)),
+                  "the only extra argument is the stamps pointer");
+    uint64_t ts_start = 0, ts_staged = 0;
+    if constexpr (STAMP) ts_start = stamp_now();
     constexpr int LPG = GS * BITS / 128;          // lanes (chunks) per group
     constexpr int VPC = 128 / BITS;               // values per chunk
     constexpr int XCB = VPC * (XF32 ? 4 : 2);     // activation bytes per chunk in LDS
@@ -672,8 +713,10 @@ void qmv_affine_kernel(const Params p)
     const float2* SClds = reinterpret_cast<const float2*>(lds + p.s_off);
     const int cwin = p.win_steps * kWave;                  // chunks per window
 
-    if ((int)blockIdx.x >= p.n_rb) return;
-    const int n_my = (p.n_rb - 1 - (int)blockIdx.x) / grid + 1;   // row blocks of this workgroup
+    // (The grid never exceeds the row blocks, so every workgroup has one; a
+    // test of that here would cost a round trip to the kernel arguments
+    // before the others are requested.)
+    const int n_my = p.rb_per - ((int)blockIdx.x >= p.rb_full ? 1 : 0);   // row blocks of this workgroup
     const int n_units = n_my * p.nsteps;
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(p.x, M * p.K * (XF32 ? 4 : 2));
 
@@ -762,7 +805,7 @@ void qmv_affine_kernel(const Params p)
     }
     auto load_meta = [&]() {
         const int sp = p.m_slot >> 4;
-        const int b = lane / sp;
+        const int b = (lane * p.m_div) >> 13;   // lane / sp (exact for lane < 64, sp <= 64)
         const int pc = lane - b * sp;
         const int bb = min(b, n_my - 1);
         const int r0 = min((((int)blockIdx.x + bb * grid) * W + wave) * R, p.N - 1);
@@ -774,6 +817,7 @@ void qmv_affine_kernel(const Params p)
 
     const uint32_t magic = opaque_u32(code_magic<BITS>());
     Stager<BITS, GS, M, XF32> stg;
+    stg.nthr = W * kWave;
     uint4 wb[NS][R];
     unsigned short sb[NS][RL], bb[NS][RL];  // scale and bias bits (of the lane's own rows with OWNLOAD)
     auto prologue = [&]() {
@@ -787,6 +831,7 @@ void qmv_affine_kernel(const Params p)
         prologue();
     });
     __syncthreads();
+    if constexpr (STAMP) ts_staged = stamp_now();
 
     float acc[RS][M];
 #pragma unroll
@@ -1210,6 +1255,21 @@ void qmv_affine_kernel(const Params p)
                     ++c_tw;
                 }
             }
+        }
+    }
+    if constexpr (STAMP) {
+        const uint64_t ts_end = stamp_now();
+        const uint32_t xcc = __builtin_amdgcn_s_getreg(0xf814);   // hwreg(HW_REG_XCC_ID)
+        const uint32_t hwid = __builtin_amdgcn_s_getreg(0xf804);  // hwreg(HW_REG_HW_ID)
+        // lane 0, from the lane count (the lane id in a register of its own
+        // would stay live through the unit loop)
+        if (__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) == 0) {
+            uint64_t* const stamps[] = {stamp_ptr...};
+            uint64_t* o = stamps[0] + ((size_t)blockIdx.x * W + wave) * kStamps;
+            o[0] = ts_start;
+            o[1] = ts_staged;
+            o[2] = ts_end;
+            o[3] = ((uint64_t)xcc << 32) | hwid;
         }
     }
 }

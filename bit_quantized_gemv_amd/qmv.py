@@ -29,6 +29,15 @@ class KernelInfo(ctypes.Structure):
                                              "k_windows", "prefetch_units", "meta_lds")]
 
 
+STAMPS = 4        # values per wavefront written by the stamped launch
+
+
+class TimelineInfo(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int) for n in ("waves", "wg_size", "grid", "clock_khz",
+                                             "blocks_per_cu", "product_blocks_per_cu",
+                                             "vgprs", "product_vgprs")]
+
+
 _lib = None
 
 
@@ -57,6 +66,9 @@ def lib():
         L.qmv_stream_read_ex.restype = I
         L.qmv_mxfp4.argtypes = [P, P, P, P, I, I, I, I, I, P]
         L.qmv_mxfp4.restype = I
+        L.qmv_affine_timeline.argtypes = [P, P, P, P, P, I, I, I, I, I, P, ctypes.c_longlong,
+                                          ctypes.POINTER(TimelineInfo), P]
+        L.qmv_affine_timeline.restype = I
         _lib = L
     return _lib
 
@@ -181,6 +193,53 @@ def affine(w, scales, biases, x, *, bits: int, group_size: int, out=None, out_dt
     if status != 0:
         raise QmvError(status, "qmv_affine_ex")
     return out[0] if squeeze else out
+
+
+def timeline_ptr(w, s, b, x, y, M, N, K, y_dt, rows_per_wave, stamps, stamps_len, info,
+                 stream=0) -> int:
+    """Raw C-ABI call of the stamped launch (a measurement aid); info is a
+    TimelineInfo filled by the call; stamps may be 0 (no launch)."""
+    return lib().qmv_affine_timeline(w, s, b, x, y, M, N, K, y_dt, rows_per_wave, stamps,
+                                     stamps_len, ctypes.byref(info), stream)
+
+
+def timeline(w, scales, biases, x, *, rows_per_wave: int = 0, out=None, out_dtype=None,
+             stream=None):
+    """The one launch `affine` makes for 4-bit codes, group size 64, bf16
+    activations and bf16 scales/biases, run with per-wavefront stamps (a
+    measurement aid).  Returns (y, stamps, info): y as `affine` returns it;
+    stamps an int64 [waves][STAMPS] tensor on the device (start, activations
+    staged, end -- in ticks of info["clock_khz"] per ms -- and
+    (XCC id << 32) | HW_ID); info the launch's fields (TimelineInfo).
+    """
+    import torch
+    if x.dim() != 2 or w.dim() != 2:
+        raise ValueError("x must be [M][K] and w [N][K/8]")
+    if x.dtype != torch.bfloat16 or scales.dtype != torch.bfloat16 or biases.dtype != torch.bfloat16:
+        raise TypeError("the stamped launch takes bf16 activations, scales and biases")
+    if w.dtype not in (torch.int32, torch.uint32):
+        raise TypeError("w must be int32 or uint32 packed words")
+    M, K = x.shape
+    N = w.shape[0]
+    if K % 64 != 0:
+        raise ValueError(f"K = {K} is not a multiple of 64")
+    _expect(w, (N, K // 8), "w")
+    _expect(scales, (N, K // 64), "scales")
+    _expect(biases, (N, K // 64), "biases")
+    _check_tensors(((w, "w"), (scales, "scales"), (biases, "biases"), (x, "x")))
+    out = _out_for(out, out_dtype, M, N, x, torch)
+    info = TimelineInfo()
+    args = (w.data_ptr(), scales.data_ptr(), biases.data_ptr(), x.data_ptr(), out.data_ptr(),
+            M, N, K, _dt_of(out, "out"), rows_per_wave)
+    status = timeline_ptr(*args, None, 0, info)
+    if status != 0:
+        raise QmvError(status, "qmv_affine_timeline")
+    stamps = torch.zeros((info.waves, STAMPS), dtype=torch.int64, device=x.device)
+    st = torch.cuda.current_stream(x.device) if stream is None else stream
+    status = timeline_ptr(*args, stamps.data_ptr(), stamps.numel(), info, st.cuda_stream)
+    if status != 0:
+        raise QmvError(status, "qmv_affine_timeline")
+    return out, stamps, {n: getattr(info, n) for n, _ in TimelineInfo._fields_}
 
 
 def _check_tensors(named):

@@ -181,6 +181,49 @@ int qmv_stream_read(const void* buf, long long bytes, uint32_t* out, int checksu
 int qmv_stream_read_ex(const void* buf, long long bytes, uint32_t* out, int checksum,
                        int wg_per_cu, int waves_per_wg, int batch, int interleave, void* stream);
 
+/* Measurement aid, not part of the product: the one launch qmv_affine_ex
+ * makes for these arguments with 4-bit codes, group size 64, bf16 activations
+ * and bf16 scales and biases (the library's choice of launch, or
+ * rows_per_wave as there), run by the same kernel with per-wavefront stamps
+ * added.  y is written exactly as qmv_affine_ex writes it.  For wavefront
+ * w = workgroup * (wg_size / 64) + wavefront-in-workgroup, lane 0 writes
+ * QMV_STAMPS values to stamps[w * QMV_STAMPS ...]: the device's constant-rate
+ * counter (s_memrealtime, clock_khz ticks per millisecond) at the wavefront's
+ * start, once its activations are staged (after the workgroup barrier), and
+ * at its end; then (XCC id << 32) | HW_ID, the hardware register that names
+ * the wavefront's compute unit (bits 8..11), shader array (bit 12), shader
+ * engine (bits 13..15) and SIMD (bits 4..5).  Nothing is stamped inside the
+ * unit loop, whose code stays the product's; each counter read waits for its
+ * own result (and any LDS or scalar load still in flight), so the stamped
+ * kernel runs as the product one does, give or take three such reads and one
+ * 32-byte store per wavefront.
+ *   stamps: device memory, 8-byte aligned, stamps_len >= waves * QMV_STAMPS
+ *   entries, not overlapping any other buffer; NULL only fills *info (no
+ *   launch).  info (host memory, required): waves and grid of the launch,
+ *   wg_size (threads), clock_khz, and resident workgroups per compute unit and
+ *   VGPRs of the stamped instance beside those of the product instance (equal
+ *   when the stamps change nothing of the launch's residency).
+ * M must be in [1, QMV_TILE_M] and the call one launch (else QMV_E_M_RANGE);
+ * other errors as for qmv_affine_ex, plus QMV_E_SHAPE for too few stamps,
+ * QMV_E_ALIGN and QMV_E_ALIAS for the stamps buffer.  Asynchronous on
+ * `stream`; the stamps are valid once it has been synchronized. */
+#define QMV_STAMPS 4
+typedef struct {
+    int waves;
+    int wg_size;
+    int grid;
+    int clock_khz;
+    int blocks_per_cu;
+    int product_blocks_per_cu;
+    int vgprs;
+    int product_vgprs;
+} qmv_timeline_info_t;
+
+int qmv_affine_timeline(const uint32_t* w_packed, const void* scales, const void* biases,
+                        const void* x, void* y, int M, int N, int K, qmv_dtype y_dt,
+                        int rows_per_wave, uint64_t* stamps, long long stamps_len,
+                        qmv_timeline_info_t* info, void* stream);
+
 /*
  * mxfp4 mode: y = qmv(x) with FP4 (E2M1) codes and one E8M0 scale per block of
  * 32 values along K, no bias:

@@ -26,8 +26,9 @@ def L():
 
 
 def test_header_declares_the_boundary():
-    assert declared_functions() == ["qmv_affine", "qmv_affine_ex", "qmv_kernel_info", "qmv_mxfp4",
-                                    "qmv_status_string", "qmv_stream_read", "qmv_stream_read_ex"]
+    assert declared_functions() == ["qmv_affine", "qmv_affine_ex", "qmv_affine_timeline",
+                                    "qmv_kernel_info", "qmv_mxfp4", "qmv_status_string",
+                                    "qmv_stream_read", "qmv_stream_read_ex"]
 
 
 def test_exports_every_declared_symbol(L):
@@ -88,6 +89,30 @@ def test_kernel_info_validates(L):
     assert L.qmv_kernel_info(1, 256, 512, 4, 64, 2, 0, 2, 0, ctypes.byref(info)) == 7   # sb_dt f32
     assert L.qmv_kernel_info(1, 256, 512, 4, 64, 2, 2, 1, 0, ctypes.byref(info)) == 7   # y_dt f16
     assert L.qmv_kernel_info(1, 256, 512, 4, 64, 2, 2, 2, 5, ctypes.byref(info)) == 8
+
+
+def test_timeline_validates(L):
+    # the stamped launch: pure host checks, in the header's order, before any HIP call
+    from bit_quantized_gemv_amd import qmv
+    info = qmv.TimelineInfo()
+    ST = A + 5 * S
+
+    def tl(w=W, s=SC, b=BI, x=X, y=Y, M=1, N=256, K=512, ydt=2, R=0, st=ST, n=1 << 20, inf=info):
+        return L.qmv_affine_timeline(w, s, b, x, y, M, N, K, ydt, R, st, n,
+                                     None if inf is None else ctypes.byref(inf), None)
+    assert tl(inf=None) == 1                       # QMV_E_NULL: info is required
+    assert tl(w=0) == 1
+    assert tl(K=96) == 4                           # not a multiple of the group size 64
+    assert tl(M=0) == 5 and tl(M=14) == 5          # one launch of at most 13 vectors
+    assert tl(x=X + 8) == 6
+    assert tl(ydt=1) == 7
+    assert tl(R=5) == 8
+    assert tl(y=X) == 9
+    assert tl(st=ST + 4) == 6                      # stamps 8-byte aligned
+    assert tl(n=0) == 4                            # an empty stamps buffer
+    assert tl(st=Y) == 9 and tl(st=W + 8) == 9     # stamps overlap y / the weights
+    # the checks end here: the next step asks the runtime for the device
+    # (QMV_E_LAUNCH without a GPU)
 
 
 def _tensors(N=4, K=512, bits=4, gs=64, M=1):
