@@ -52,6 +52,8 @@ struct MxParams {
     int win_steps;   // wave steps per K window (even unless one window covers K)
     int nwin;        // K windows
     int xm_bytes;    // LDS bytes of one vector's window (win_steps*64 chunks of 64 B, padded)
+    uint32_t ipm_magic;  // i / (16-byte pieces per vector and window) is
+    int ipm_shift;       // umulhi(i, ipm_magic) >> ipm_shift for every staging index i
 };
 
 // 2^(E - 127) as fp32 from an E8M0 byte: E = 0 is the subnormal 2^-127 and
@@ -103,7 +105,8 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void qmv_mx_kernel(MxParams p)
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
     const int W = blockDim.x / kWave;
     const int grid = gridDim.x;
-    if ((int)blockIdx.x >= p.n_rb) return;
+    // (the grid never exceeds the row blocks, so every workgroup has one; a
+    // test of that here would hold back the other argument loads)
 
     const __amdgpu_buffer_rsrc_t wr = make_rsrc(p.w, -1);
     const __amdgpu_buffer_rsrc_t sr = make_rsrc(p.s, -1);
@@ -140,7 +143,7 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void qmv_mx_kernel(MxParams p)
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int i = min(i0 + j * (int)blockDim.x + (int)threadIdx.x, items - 1);
-                const int m = i / (cwin * PPC), rem = i - m * (cwin * PPC);
+                const int m = (int)(__umulhi((uint32_t)i, p.ipm_magic) >> p.ipm_shift), rem = i - m * (cwin * PPC);
                 const int c = min(c0 + (rem >> PSH), p.chunks - 1), piece = rem & (PPC - 1);
                 v[j] = buf_load(xr, (m * p.K + c * 32) * XB + piece * 16);
             }
@@ -149,7 +152,7 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void qmv_mx_kernel(MxParams p)
             for (int j = 0; j < 8; ++j) {
                 const int i = i0 + j * (int)blockDim.x + (int)threadIdx.x;
                 if (i < items) {
-                    const int m = i / (cwin * PPC), rem = i - m * (cwin * PPC);
+                    const int m = (int)(__umulhi((uint32_t)i, p.ipm_magic) >> p.ipm_shift), rem = i - m * (cwin * PPC);
                     const int cl = rem >> PSH, piece = rem & (PPC - 1);
                     const uint4 d = (c0 + cl < p.chunks) ? v[j] : make_uint4(0, 0, 0, 0);
                     *reinterpret_cast<uint4*>(lds + m * p.xm_bytes + lds_phys(cl * CB + piece * 16)) = d;
@@ -469,6 +472,19 @@ extern "C" int qmv_mxfp4(const uint32_t* w_packed, const uint8_t* scales, const 
         p.win_steps = win ? shape.win_steps : p.nsteps;
         p.nwin = (p.nsteps + p.win_steps - 1) / p.win_steps;
         p.xm_bytes = p.win_steps * step_bytes;
+        {
+            // exact division by d = pieces per vector and window for every
+            // index below 2^21 (at most 13 * 2^14 here): with k >= 21 +
+            // ceil(log2 d) and magic = ceil(2^k / d), i * d < 2^k makes
+            // floor(i * magic / 2^k) = floor(i / d); k >= 32 keeps it one
+            // high-half multiply, and magic < 2^32
+            const uint32_t d = (uint32_t)p.win_steps * qmv::kWave * (xf32 ? 8u : 4u);
+            int lg = 0;
+            while ((1u << lg) < d) ++lg;
+            const int k = std::max(32, 21 + lg);
+            p.ipm_shift = k - 32;
+            p.ipm_magic = (uint32_t)(((1ULL << k) + d - 1) / d);
+        }
         const int lds = Mt * p.xm_bytes;
         if (lds > kMxLds) return QMV_E_SHAPE;
         const MxKernelFn fn = mx_kernel(R, Mt, win, xf32);
