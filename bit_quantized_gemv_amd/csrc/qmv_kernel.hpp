@@ -479,6 +479,8 @@ struct Stager {
                     ++m;
                 }
             }
+            // (more vectors: nothing of `between` moves above the loads)
+            if constexpr (M != 1) __builtin_amdgcn_sched_barrier(0);
             between();
             m = 0;
             j = 0;
@@ -753,7 +755,11 @@ void qmv_affine_kernel(const Params p, Stamps... stamp_ptr)
             for (int k = 0; k < RL; ++k) i_ps[k] = min(k * LPG + lane % LPG, p.N - 1 - rbase) * p.G * 2;
         }
     };
-    set_block();
+    // One vector: the row block's resources first, so that the first weight
+    // requests follow the activation loads at once.  More vectors: the
+    // activation loads first (their staging is the longer wait), the
+    // resources while they are in flight.
+    if constexpr (M == 1) set_block();
     const int wo0 = lane * 16;                       // lane's chunk offset in a row's first step
     const int mo0 = (lane / LPG) * 2;                // lane's group offset in a row's first step
     int i_wo = wo0, i_mo = mo0;
@@ -827,6 +833,7 @@ void qmv_affine_kernel(const Params p, Stamps... stamp_ptr)
     // activation loads first, then (whole K) the scale/bias pieces, then the
     // weight prologue, then the conversion
     stg.stage(p, xr, lds, 0, [&]() {
+        if constexpr (M != 1) set_block();
         if constexpr (MLDS) load_meta();
         prologue();
     });
