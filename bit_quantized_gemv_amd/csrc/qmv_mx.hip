@@ -135,13 +135,17 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void qmv_mx_kernel(MxParams p)
     constexpr int PPC = 1 << PSH;
     constexpr int CB = 32 * XB;                           // LDS bytes per chunk
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(p.x, M * p.K * XB);
+    // 16-byte pieces per thread and batch: a window of one or two vectors has
+    // few per thread, and the clamped re-reads that fill a larger batch cost
+    // more than the second batch a long window then needs
+    constexpr int SB = (M == 1) ? 2 : (M == 2 ? 4 : 8);
     auto stage = [&](int win, auto first_tag) {
         const int items = M * cwin * PPC;
         const int c0 = win * cwin;
         auto batch = [&](int i0, auto with_issue) {
-            uint4 v[8];
+            uint4 v[SB];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
+            for (int j = 0; j < SB; ++j) {
                 const int i = min(i0 + j * (int)blockDim.x + (int)threadIdx.x, items - 1);
                 const int m = (int)(__umulhi((uint32_t)i, p.ipm_magic) >> p.ipm_shift), rem = i - m * (cwin * PPC);
                 const int c = min(c0 + (rem >> PSH), p.chunks - 1), piece = rem & (PPC - 1);
@@ -149,7 +153,7 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void qmv_mx_kernel(MxParams p)
             }
             if constexpr (decltype(with_issue)::value) issue(0, blockIdx.x, 0);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
+            for (int j = 0; j < SB; ++j) {
                 const int i = i0 + j * (int)blockDim.x + (int)threadIdx.x;
                 if (i < items) {
                     const int m = (int)(__umulhi((uint32_t)i, p.ipm_magic) >> p.ipm_shift), rem = i - m * (cwin * PPC);
@@ -160,7 +164,7 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void qmv_mx_kernel(MxParams p)
             }
         };
         batch(0, first_tag);
-        for (int i0 = 8 * (int)blockDim.x; i0 < items; i0 += 8 * (int)blockDim.x) batch(i0, std::false_type{});
+        for (int i0 = SB * (int)blockDim.x; i0 < items; i0 += SB * (int)blockDim.x) batch(i0, std::false_type{});
     };
     if constexpr (!WIN) {
         stage(0, std::true_type{});
