@@ -40,7 +40,11 @@ Other modes (one JSON line per point instead of the bench line):
                      mxfp4 mode on the four projection shapes
     --sweep-rows     rows per wavefront 1-4 at M = 1, 4, 8, 13 on the 27B-class
                      shapes, with VGPRs, LDS, grid and wavefronts per SIMD
-    --sweep-ceiling  the streaming-read ceiling over the launch shape
+    --sweep-ceiling  the streaming-read ceiling over the launch shape, at the
+                     4-bit and the 2-bit one-vector byte counts
+    --timeline       per-wavefront timelines of the 4-bit projection shapes at
+                     M = 1 and 13 (stamped instance of the same kernel), with
+                     cold and cache-hot activations
 """
 from __future__ import annotations
 
@@ -352,41 +356,50 @@ def sweep_rows(args, q, gen, torch, np, dev):
 
 
 def sweep_ceiling(args, q, gen, torch, np, dev):
-    """The streaming-read ceiling over the bench line's byte count (33,216,000
-    B), same rotation and timing, swept over the launch shape: workgroups per
-    compute unit, wavefronts per workgroup, loads in flight per lane, and
-    contiguous or interleaved spans.  One JSON line per shape."""
-    p = gen.make_problem(WORKLOAD)
-    nb = alg_bytes(p.N, p.K, p.bits, p.gs, 1)
-    nc = max(2, -(-ROTATE_BYTES // nb))
-    bufs = [torch.empty(nb, dtype=torch.uint8, device=dev).random_(0, 256) for _ in range(nc)]
-    sink = torch.zeros(1, dtype=torch.int32, device=dev)
-    shape = [4, 8, 4, 0]
+    """The streaming-read ceiling over the one-vector byte counts of the bench
+    line's workload (33,216,000 B) and of the 2-bit 15360 x 3840 workload
+    (16,627,200 B), same rotation and timing, swept over the launch shape:
+    workgroups per compute unit, wavefronts per workgroup, loads in flight per
+    lane, and contiguous or interleaved spans.  One JSON line per shape, then
+    the best shape of each byte count."""
+    settled = False
+    for name in (WORKLOAD, "up_2b_15360x3840"):
+        p = gen.make_problem(name)
+        nb = alg_bytes(p.N, p.K, p.bits, p.gs, 1)
+        nc = max(2, -(-ROTATE_BYTES // nb))
+        bufs = [torch.empty(nb, dtype=torch.uint8, device=dev).random_(0, 256) for _ in range(nc)]
+        sink = torch.zeros(1, dtype=torch.int32, device=dev)
+        shape = [4, 8, 4, 0]
 
-    def launch(i, M, stream):
-        st = q.stream_read_ex_ptr(bufs[i].data_ptr(), nb, sink.data_ptr(), *shape,
-                                  stream=stream.cuda_stream)
-        if st != 0:
-            raise q.QmvError(st, "qmv_stream_read_ex")
+        def launch(i, M, stream):
+            st = q.stream_read_ex_ptr(bufs[i].data_ptr(), nb, sink.data_ptr(), *shape,
+                                      stream=stream.cuda_stream)
+            if st != 0:
+                raise q.QmvError(st, "qmv_stream_read_ex")
 
-    settle_clocks(launch, nc, torch)
-    best = None
-    for wg in (1, 2, 4, 8, 16):
-        for waves in (4, 8, 16):
-            if wg * waves > 32 * 4:
-                continue
-            for batch in (1, 2, 4, 8, 16):
-                for inter in (0, 1):
-                    shape[:] = [wg, waves, batch, inter]
-                    us, _ = time_calls(launch, nc, 1, args.steps, args.warmup, torch)
-                    gbs = nb / (us * 1e-6) / 1e9
-                    rec = {"sweep": "stream_ceiling", "bytes": nb, "wg_per_cu": wg, "waves_per_wg": waves,
-                           "batch": batch, "interleave": inter, "us_per_call": round(us, 3),
-                           "GB/s": round(gbs, 1), "frac_of_peak": round(gbs / PEAK_GBS, 4)}
-                    print(json.dumps(rec), flush=True)
-                    if best is None or us < best["us_per_call"]:
-                        best = rec
-    print(json.dumps({"sweep": "stream_ceiling_best", **best}), flush=True)
+        if not settled:
+            settle_clocks(launch, nc, torch)
+            settled = True
+        best = None
+        for wg in (1, 2, 4, 8, 16):
+            for waves in (4, 8, 16):
+                if wg * waves > 32 * 4:
+                    continue
+                for batch in (1, 2, 4, 8, 16):
+                    for inter in (0, 1):
+                        shape[:] = [wg, waves, batch, inter]
+                        us, _ = time_calls(launch, nc, 1, args.steps, args.warmup, torch)
+                        gbs = nb / (us * 1e-6) / 1e9
+                        rec = {"sweep": "stream_ceiling", "workload": name, "bytes": nb, "wg_per_cu": wg,
+                               "waves_per_wg": waves, "batch": batch, "interleave": inter,
+                               "us_per_call": round(us, 3), "GB/s": round(gbs, 1),
+                               "frac_of_peak": round(gbs / PEAK_GBS, 4)}
+                        print(json.dumps(rec), flush=True)
+                        if best is None or us < best["us_per_call"]:
+                            best = rec
+        print(json.dumps({**best, "sweep": "stream_ceiling_best"}), flush=True)
+        del bufs
+        torch.cuda.empty_cache()
 
 
 def _pcts(v, np):
@@ -525,7 +538,8 @@ def main():
                     help="instead of the bench line, time rows per wavefront 1-4 at M = 1, 4, 8, 13 on "
                          "the 27B-class shapes, with resources and occupancy per point")
     ap.add_argument("--sweep-ceiling", action="store_true",
-                    help="instead of the bench line, sweep the streaming-read ceiling's launch shape")
+                    help="instead of the bench line, sweep the streaming-read ceiling's launch shape "
+                         "over the 4-bit and 2-bit one-vector byte counts")
     ap.add_argument("--timeline", action="store_true",
                     help="instead of the bench line, per-wavefront timelines of the 4-bit projection "
                          "shapes at M = 1 and 13 (stamped instance of the same kernel)")
