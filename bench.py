@@ -439,7 +439,7 @@ def _timeline_stats(bufs, clock_khz, np):
 def timeline(args, q, gen, torch, np, dev):
     """Per-wavefront timeline of the library's launch, from the stamped
     instance of the same kernel (qmv_affine_timeline): the 4-bit group-64
-    projection shapes at M = 1 and 13.  Each sample is one stamped call on a
+    projection shapes at M = 1 and 13 (--timeline-m to choose).  Each sample is one stamped call on a
     rotating copy, enqueued right after a few product calls on other copies
     (so the GPU is busy and the copy cold in the caches, as in the timed
     bench); per sample the stamps are taken relative to its earliest wavefront
@@ -466,7 +466,7 @@ def timeline(args, q, gen, torch, np, dev):
         if not settled:
             settle_clocks(affine_launcher(q, p, ptrs), nc, torch)
             settled = True
-        for M in (1, 13):
+        for M in args.timeline_m:
             # a call cut into tiles of vectors is stamped on its first tile
             info = q.TimelineInfo()
             while True:
@@ -543,6 +543,8 @@ def main():
     ap.add_argument("--timeline", action="store_true",
                     help="instead of the bench line, per-wavefront timelines of the 4-bit projection "
                          "shapes at M = 1 and 13 (stamped instance of the same kernel)")
+    ap.add_argument("--timeline-m", type=lambda v: tuple(int(t) for t in v.split(",")), default=(1, 13),
+                    help="vector counts of --timeline, comma-separated (default 1,13)")
     args = ap.parse_args()
 
     if args.gpus != 1:
