@@ -659,10 +659,12 @@ __device__ __forceinline__ uint64_t stamp_now()
 // Stamps: the product instances take no further argument (Stamps empty).  The
 // measurement instance takes one, a uint64_t* to which lane 0 of each
 // wavefront writes its kStamps values at stamps[(workgroup * W + wave) *
-// kStamps ...] after its last unit; its code is the product's with the three
-// counter reads, two hardware-register reads and that store added.  (The stamps stay inside this one
+// kStamps ...] after its last unit; its code is the product's with three
+// counter reads, two hardware-register reads and that store added (the
+// scheduling barriers around the counter reads keep some of the product's
+// setup instructions on their side).  The stamps stay inside this one
 // definition: a kernel body moved into a device function compiles to
-// different code.)
+// different code.
 template <int BITS, int GS, int R, int M, int PF, bool XF32, bool SBF, bool WIN, class... Stamps>
 __global__ __launch_bounds__(kMaxWaves * kWave) __attribute__((amdgpu_waves_per_eu(waves_hint(BITS, XF32, R, M, PF, WIN))))
 void qmv_affine_kernel(const Params p, Stamps... stamp_ptr)
