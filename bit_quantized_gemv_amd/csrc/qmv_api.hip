@@ -516,6 +516,7 @@ int qmv_affine_timeline(const uint32_t* w_packed, const void* scales, const void
     st = choose_plan(M, N, K, 4, 64, false, true, rows_per_wave, pl);
     if (st != QMV_OK) return st;
     const qmv::TimelineFn tfn = qmv::qmv_timeline_b4_g64_bf16[pl.win ? 1 : 0][pl.R - 1][M - 1];
+    if (tfn == nullptr) return QMV_E_LAUNCH;
     int dev = 0, khz = 0, nb = 0, scratch = 0;
     if (hipGetDevice(&dev) != hipSuccess) return QMV_E_LAUNCH;
     if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess) return QMV_E_LAUNCH;
