@@ -439,7 +439,8 @@ def _timeline_stats(bufs, clock_khz, np):
 def timeline(args, q, gen, torch, np, dev):
     """Per-wavefront timeline of the library's launch, from the stamped
     instance of the same kernel (qmv_affine_timeline): the 4-bit group-64
-    projection shapes at M = 1 and 13 (--timeline-m to choose).  Each sample is one stamped call on a
+    projection shapes and the 2-bit group-128 up-projection at M = 1 and 13
+    (--timeline-m to choose).  Each sample is one stamped call on a
     rotating copy, enqueued right after a few product calls on other copies
     (so the GPU is busy and the copy cold in the caches, as in the timed
     bench); per sample the stamps are taken relative to its earliest wavefront
@@ -457,7 +458,8 @@ def timeline(args, q, gen, torch, np, dev):
     is stamped on its first tile's vectors.  One JSON line per point."""
     samples = max(5, min(args.steps, 50))
     settled = False
-    for name in ("up_4b_15360x3840", "down_4b_3840x15360", "up_4b_17408x5120", "down_4b_5120x17408"):
+    for name in ("up_4b_15360x3840", "down_4b_3840x15360", "up_4b_17408x5120", "down_4b_5120x17408",
+                 "up_2b_15360x3840"):
         p = gen.make_problem(name)
         N, K, bits, gs = p.N, p.K, p.bits, p.gs
         nc = max(2, -(-ROTATE_BYTES // alg_bytes(N, K, bits, gs, 13)))
@@ -470,7 +472,7 @@ def timeline(args, q, gen, torch, np, dev):
             # a call cut into tiles of vectors is stamped on its first tile
             info = q.TimelineInfo()
             while True:
-                st = q.timeline_ptr(*ptrs[0][:5], M, N, K, q.DT_BF16, 0, None, 0, info)
+                st = q.timeline_ptr(*ptrs[0][:5], M, N, K, bits, gs, q.DT_BF16, 0, None, 0, info)
                 if st != 5 or M == 1:
                     break
                 M -= 1
@@ -482,8 +484,8 @@ def timeline(args, q, gen, torch, np, dev):
             def stamped_launcher(pp):
                 def launch_stamped(i, M, stream, buf=None):
                     b = bufs[0] if buf is None else buf
-                    st = q.timeline_ptr(*pp[i][:5], M, N, K, q.DT_BF16, 0, b.data_ptr(), b.numel(),
-                                        info, stream.cuda_stream)
+                    st = q.timeline_ptr(*pp[i][:5], M, N, K, bits, gs, q.DT_BF16, 0, b.data_ptr(),
+                                        b.numel(), info, stream.cuda_stream)
                     if st != 0:
                         raise q.QmvError(st, "qmv_affine_timeline")
                 return launch_stamped

@@ -489,33 +489,36 @@ int qmv_kernel_info(int M, int N, int K, int bits, int group_size, qmv_dtype x_d
 }
 
 int qmv_affine_timeline(const uint32_t* w_packed, const void* scales, const void* biases,
-                        const void* x, void* y, int M, int N, int K, qmv_dtype y_dt,
-                        int rows_per_wave, uint64_t* stamps, long long stamps_len,
+                        const void* x, void* y, int M, int N, int K, int bits, int group_size,
+                        qmv_dtype y_dt, int rows_per_wave, uint64_t* stamps, long long stamps_len,
                         qmv_timeline_info_t* info, void* stream)
 {
     if (!info) return QMV_E_NULL;
-    int st = check_args(w_packed, scales, biases, x, y, M, N, K, 4, 64, QMV_DT_BF16, QMV_DT_BF16,
-                        y_dt, rows_per_wave);
+    int st = check_args(w_packed, scales, biases, x, y, M, N, K, bits, group_size, QMV_DT_BF16,
+                        QMV_DT_BF16, y_dt, rows_per_wave);
     if (st != QMV_OK) return st;
+    // the stamped sets: 4-bit codes in groups of 64, 2-bit codes in groups of 128
+    if ((bits == 4) != (group_size == 64)) return QMV_E_GROUP;
     if (M > QMV_TILE_M) return QMV_E_M_RANGE;
     if (stamps && !aligned(stamps, 8)) return QMV_E_ALIGN;
     if (stamps && stamps_len < 1) return QMV_E_SHAPE;
     if (stamps) {
         const size_t nst = (size_t)stamps_len * 8;
-        const size_t nw = (size_t)N * (size_t)K / 2, nsb = (size_t)N * (size_t)(K / 64) * 2;
+        const size_t nw = (size_t)N * (size_t)K * bits / 8, nsb = (size_t)N * (size_t)(K / group_size) * 2;
         const size_t nx = (size_t)M * (size_t)K * 2, ny = (size_t)M * (size_t)N * dtype_bytes(y_dt);
         if (overlap(stamps, nst, w_packed, nw) || overlap(stamps, nst, scales, nsb) ||
             overlap(stamps, nst, biases, nsb) || overlap(stamps, nst, x, nx) || overlap(stamps, nst, y, ny))
             return QMV_E_ALIAS;
     }
     // the call must be the one launch qmv_affine_ex would make
-    const int mc = tile_vectors(M, N, K, 4, 64, false, true, rows_per_wave);
+    const int mc = tile_vectors(M, N, K, bits, group_size, false, true, rows_per_wave);
     if (mc < 1) return QMV_E_SHAPE;
     if (mc < M) return QMV_E_M_RANGE;
     Plan pl;
-    st = choose_plan(M, N, K, 4, 64, false, true, rows_per_wave, pl);
+    st = choose_plan(M, N, K, bits, group_size, false, true, rows_per_wave, pl);
     if (st != QMV_OK) return st;
-    const qmv::TimelineFn tfn = qmv::qmv_timeline_b4_g64_bf16[pl.win ? 1 : 0][pl.R - 1][M - 1];
+    const qmv::TimelineFn tfn = (bits == 4 ? qmv::qmv_timeline_b4_g64_bf16
+                                           : qmv::qmv_timeline_b2_g128_bf16)[pl.win ? 1 : 0][pl.R - 1][M - 1];
     if (tfn == nullptr) return QMV_E_LAUNCH;
     int dev = 0, khz = 0, nb = 0, scratch = 0;
     if (hipGetDevice(&dev) != hipSuccess) return QMV_E_LAUNCH;

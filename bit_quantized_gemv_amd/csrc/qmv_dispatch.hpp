@@ -32,10 +32,11 @@ extern const KernelFn qmv_wtable_b2_g64_f32[kNumR][kMaxM][kNumSb];
 extern const KernelFn qmv_wtable_b2_g128_bf16[kNumR][kMaxM][kNumSb];
 extern const KernelFn qmv_wtable_b2_g128_f32[kNumR][kMaxM][kNumSb];
 
-// Stamped instances (measurement aid): 4-bit codes, groups of 64, bf16
-// activations and bf16 scales/biases, indexed [K-windowed][rows per
-// wavefront - 1][M - 1].
+// Stamped instances (measurement aid): bf16 activations and bf16
+// scales/biases, 4-bit codes in groups of 64 and 2-bit codes in groups of
+// 128, indexed [K-windowed][rows per wavefront - 1][M - 1].
 using TimelineFn = void (*)(Params, uint64_t*);
 extern const TimelineFn qmv_timeline_b4_g64_bf16[2][kNumR][kMaxM];
+extern const TimelineFn qmv_timeline_b2_g128_bf16[2][kNumR][kMaxM];
 
 }  // namespace qmv

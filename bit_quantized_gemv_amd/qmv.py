@@ -66,7 +66,7 @@ def lib():
         L.qmv_stream_read_ex.restype = I
         L.qmv_mxfp4.argtypes = [P, P, P, P, I, I, I, I, I, P]
         L.qmv_mxfp4.restype = I
-        L.qmv_affine_timeline.argtypes = [P, P, P, P, P, I, I, I, I, I, P, ctypes.c_longlong,
+        L.qmv_affine_timeline.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, P, ctypes.c_longlong,
                                           ctypes.POINTER(TimelineInfo), P]
         L.qmv_affine_timeline.restype = I
         _lib = L
@@ -195,42 +195,45 @@ def affine(w, scales, biases, x, *, bits: int, group_size: int, out=None, out_dt
     return out[0] if squeeze else out
 
 
-def timeline_ptr(w, s, b, x, y, M, N, K, y_dt, rows_per_wave, stamps, stamps_len, info,
-                 stream=0) -> int:
+def timeline_ptr(w, s, b, x, y, M, N, K, bits, group_size, y_dt, rows_per_wave, stamps,
+                 stamps_len, info, stream=0) -> int:
     """Raw C-ABI call of the stamped launch (a measurement aid); info is a
     TimelineInfo filled by the call; stamps may be 0 (no launch)."""
-    return lib().qmv_affine_timeline(w, s, b, x, y, M, N, K, y_dt, rows_per_wave, stamps,
-                                     stamps_len, ctypes.byref(info), stream)
+    return lib().qmv_affine_timeline(w, s, b, x, y, M, N, K, bits, group_size, y_dt,
+                                     rows_per_wave, stamps, stamps_len, ctypes.byref(info), stream)
 
 
-def timeline(w, scales, biases, x, *, rows_per_wave: int = 0, out=None, out_dtype=None,
-             stream=None):
-    """The one launch `affine` makes for 4-bit codes, group size 64, bf16
-    activations and bf16 scales/biases, run with per-wavefront stamps (a
-    measurement aid).  Returns (y, stamps, info): y as `affine` returns it;
+def timeline(w, scales, biases, x, *, bits: int = 4, group_size: int = 64, rows_per_wave: int = 0,
+             out=None, out_dtype=None, stream=None):
+    """The one launch `affine` makes for bf16 activations and bf16
+    scales/biases with 4-bit codes in groups of 64 or 2-bit codes in groups of
+    128, run with per-wavefront stamps (a measurement aid).  Returns (y,
+    stamps, info): y as `affine` returns it;
     stamps an int64 [waves][STAMPS] tensor on the device (start, activations
     staged, end -- in ticks of info["clock_khz"] per ms -- and
     (XCC id << 32) | HW_ID); info the launch's fields (TimelineInfo).
     """
     import torch
+    if (bits, group_size) not in ((4, 64), (2, 128)):
+        raise ValueError("the stamped launch takes 4-bit codes in groups of 64 or 2-bit in groups of 128")
     if x.dim() != 2 or w.dim() != 2:
-        raise ValueError("x must be [M][K] and w [N][K/8]")
+        raise ValueError("x must be [M][K] and w [N][K*bits/32]")
     if x.dtype != torch.bfloat16 or scales.dtype != torch.bfloat16 or biases.dtype != torch.bfloat16:
         raise TypeError("the stamped launch takes bf16 activations, scales and biases")
     if w.dtype not in (torch.int32, torch.uint32):
         raise TypeError("w must be int32 or uint32 packed words")
     M, K = x.shape
     N = w.shape[0]
-    if K % 64 != 0:
-        raise ValueError(f"K = {K} is not a multiple of 64")
-    _expect(w, (N, K // 8), "w")
-    _expect(scales, (N, K // 64), "scales")
-    _expect(biases, (N, K // 64), "biases")
+    if K % group_size != 0:
+        raise ValueError(f"K = {K} is not a multiple of {group_size}")
+    _expect(w, (N, K * bits // 32), "w")
+    _expect(scales, (N, K // group_size), "scales")
+    _expect(biases, (N, K // group_size), "biases")
     _check_tensors(((w, "w"), (scales, "scales"), (biases, "biases"), (x, "x")))
     out = _out_for(out, out_dtype, M, N, x, torch)
     info = TimelineInfo()
     args = (w.data_ptr(), scales.data_ptr(), biases.data_ptr(), x.data_ptr(), out.data_ptr(),
-            M, N, K, _dt_of(out, "out"), rows_per_wave)
+            M, N, K, bits, group_size, _dt_of(out, "out"), rows_per_wave)
     status = timeline_ptr(*args, None, 0, info)
     if status != 0:
         raise QmvError(status, "qmv_affine_timeline")

@@ -182,10 +182,10 @@ int qmv_stream_read_ex(const void* buf, long long bytes, uint32_t* out, int chec
                        int wg_per_cu, int waves_per_wg, int batch, int interleave, void* stream);
 
 /* Measurement aid, not part of the product: the one launch qmv_affine_ex
- * makes for these arguments with 4-bit codes, group size 64, bf16 activations
- * and bf16 scales and biases (the library's choice of launch, or
- * rows_per_wave as there), run by the same kernel with per-wavefront stamps
- * added.  y is written exactly as qmv_affine_ex writes it.  For wavefront
+ * makes for these arguments with bf16 activations and bf16 scales and
+ * biases, and 4-bit codes in groups of 64 or 2-bit codes in groups of 128
+ * (the library's choice of launch, or rows_per_wave as there), run by the
+ * same kernel with per-wavefront stamps added.  y is written exactly as qmv_affine_ex writes it.  For wavefront
  * w = workgroup * (wg_size / 64) + wavefront-in-workgroup, lane 0 writes
  * QMV_STAMPS values to stamps[w * QMV_STAMPS ...]: the device's constant-rate
  * counter (s_memrealtime, clock_khz ticks per millisecond) at the wavefront's
@@ -204,7 +204,8 @@ int qmv_stream_read_ex(const void* buf, long long bytes, uint32_t* out, int chec
  *   VGPRs of the stamped instance beside those of the product instance (equal
  *   when the stamps change nothing of the launch's residency).
  * M must be in [1, QMV_TILE_M] and the call one launch (else QMV_E_M_RANGE);
- * other errors as for qmv_affine_ex, plus QMV_E_SHAPE for too few stamps,
+ * QMV_E_GROUP for another pairing of bits and group size; other errors as for
+ * qmv_affine_ex, plus QMV_E_SHAPE for too few stamps,
  * QMV_E_ALIGN and QMV_E_ALIAS for the stamps buffer.  Asynchronous on
  * `stream`; the stamps are valid once it has been synchronized. */
 #define QMV_STAMPS 4
@@ -220,8 +221,8 @@ typedef struct {
 } qmv_timeline_info_t;
 
 int qmv_affine_timeline(const uint32_t* w_packed, const void* scales, const void* biases,
-                        const void* x, void* y, int M, int N, int K, qmv_dtype y_dt,
-                        int rows_per_wave, uint64_t* stamps, long long stamps_len,
+                        const void* x, void* y, int M, int N, int K, int bits, int group_size,
+                        qmv_dtype y_dt, int rows_per_wave, uint64_t* stamps, long long stamps_len,
                         qmv_timeline_info_t* info, void* stream);
 
 /*

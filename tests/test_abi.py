@@ -97,12 +97,15 @@ def test_timeline_validates(L):
     info = qmv.TimelineInfo()
     ST = A + 5 * S
 
-    def tl(w=W, s=SC, b=BI, x=X, y=Y, M=1, N=256, K=512, ydt=2, R=0, st=ST, n=1 << 20, inf=info):
-        return L.qmv_affine_timeline(w, s, b, x, y, M, N, K, ydt, R, st, n,
+    def tl(w=W, s=SC, b=BI, x=X, y=Y, M=1, N=256, K=512, bits=4, gs=64, ydt=2, R=0, st=ST, n=1 << 20,
+           inf=info):
+        return L.qmv_affine_timeline(w, s, b, x, y, M, N, K, bits, gs, ydt, R, st, n,
                                      None if inf is None else ctypes.byref(inf), None)
     assert tl(inf=None) == 1                       # QMV_E_NULL: info is required
     assert tl(w=0) == 1
     assert tl(K=96) == 4                           # not a multiple of the group size 64
+    assert tl(bits=3) == 2 and tl(gs=32) == 3
+    assert tl(bits=4, gs=128) == 3 and tl(bits=2, gs=64) == 3   # only 4-bit g64 and 2-bit g128 are stamped
     assert tl(M=0) == 5 and tl(M=14) == 5          # one launch of at most 13 vectors
     assert tl(x=X + 8) == 6
     assert tl(ydt=1) == 7

@@ -1,4 +1,5 @@
-"""GPU tests of the stamped launch (qmv_affine_timeline, a measurement aid):
+"""GPU tests of the stamped launch (qmv_affine_timeline, a measurement aid; 4-bit
+group-64 and 2-bit group-128 codes):
 its output equals the product launch's bit for bit, it keeps the product's
 launch shape and residency, and every wavefront of the grid writes ordered
 stamps from a plausible place on the chip.  Cases: the 12B- and 27B-class
@@ -25,14 +26,18 @@ CASES = [
     ((777, 2240), 5, 2),
     ((777, 2240), 5, 3),
     ((777, 2240), 5, 4),
+    ("up_2b_15360x3840", 1, 0),
+    ("up_2b_15360x3840", 13, 0),
+    ((513, 2176, 2), 3, 1),           # 2-bit, 17 groups of 128, one row per wavefront
 ]
 
 
 def _problem(spec):
     if isinstance(spec, str):
         return gen.make_problem(spec)
-    N, K = spec
-    return gen.make_problem(N=N, K=K, bits=4, gs=64, sb="bf16", x_dtype="bf16", seed=N + K)
+    N, K, bits = spec if len(spec) == 3 else (*spec, 4)
+    return gen.make_problem(N=N, K=K, bits=bits, gs=64 if bits == 4 else 128, sb="bf16",
+                            x_dtype="bf16", seed=N + K)
 
 
 @pytest.mark.parametrize("spec,M,R", CASES)
@@ -42,12 +47,13 @@ def test_timeline_matches_the_product_launch(spec, M, R):
     U.say(label)
     w, s, b, x = U.to_dev(p)
     xm = x[:M].contiguous()
-    y = U.q.affine(w, s, b, xm, bits=4, group_size=64, out_dtype=torch.float32, rows_per_wave=R)
-    yt, stamps, info = U.q.timeline(w, s, b, xm, rows_per_wave=R, out_dtype=torch.float32)
+    y = U.q.affine(w, s, b, xm, bits=p.bits, group_size=p.gs, out_dtype=torch.float32, rows_per_wave=R)
+    yt, stamps, info = U.q.timeline(w, s, b, xm, bits=p.bits, group_size=p.gs, rows_per_wave=R,
+                                    out_dtype=torch.float32)
     torch.cuda.synchronize()
     assert torch.equal(y.view(torch.int32), yt.view(torch.int32)), label
 
-    kinf = U.q.kernel_info(M, p.N, p.K, 4, 64, rows_per_wave=R)
+    kinf = U.q.kernel_info(M, p.N, p.K, p.bits, p.gs, rows_per_wave=R)
     assert info["grid"] == kinf["grid"] and info["wg_size"] == kinf["wg_size"], (info, kinf)
     assert info["waves"] == kinf["grid"] * kinf["wg_size"] // 64
     # the stamps change nothing of the launch's residency
@@ -74,13 +80,13 @@ def test_timeline_query_only():
     y = torch.full((2, p.N), 7.0, dtype=torch.float32, device=U.DEV)
     info = U.q.TimelineInfo()
     st = U.q.timeline_ptr(w.data_ptr(), s.data_ptr(), b.data_ptr(), x.data_ptr(), y.data_ptr(),
-                          2, p.N, p.K, U.q.DT_F32, 0, None, 0, info)
+                          2, p.N, p.K, 4, 64, U.q.DT_F32, 0, None, 0, info)
     torch.cuda.synchronize()
     assert st == 0 and info.waves > 0
     assert bool((y == 7.0).all())
     # too small a stamps buffer is refused before the launch
     stamps = torch.zeros(info.waves * U.q.STAMPS - 1, dtype=torch.int64, device=U.DEV)
     st = U.q.timeline_ptr(w.data_ptr(), s.data_ptr(), b.data_ptr(), x.data_ptr(), y.data_ptr(),
-                          2, p.N, p.K, U.q.DT_F32, 0, stamps.data_ptr(), stamps.numel(), info)
+                          2, p.N, p.K, 4, 64, U.q.DT_F32, 0, stamps.data_ptr(), stamps.numel(), info)
     torch.cuda.synchronize()
     assert st == 4 and bool((y == 7.0).all())
