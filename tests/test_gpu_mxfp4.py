@@ -226,3 +226,64 @@ def test_mx_graph_capture_replays_match_eager():
         torch.cuda.synchronize()
         for j in range(3):
             assert torch.equal(_bits(outs[j]), _bits(eager[j])), f"replay {i} call {j}"
+
+
+def test_mx_special_scale_exponents():
+    """E8M0 scales at the ends of the range: one block per row at E = 0 (the
+    subnormal 2^-127), 1, 2, 253 or 254 (that block's codes zero but one 0.5,
+    on an activation below 1 in magnitude, so the row stays finite); rows
+    whose every block is at E = 0..2, of which rows 15..19 hold two E = 0
+    blocks of one such 0.5 code each and nothing else (results below 2^-126,
+    which must not flush to zero); and rows with one E = 255 block, whose
+    outputs must be NaN for every vector while every other row stays finite.
+    Held to the a-priori bound of the fp32 evaluation plus one subnormal
+    spacing per rounding."""
+    N, K, M = 48, 256, 3
+    p = gen.make_mx_problem(N, K, "bf16", seed=77, keep_q=True)
+    xs, xd = _x(p, M)
+    xf = gen.bf16_bits_to_f32(xs)
+    rng = np.random.default_rng(78)
+    q, e = p.q.copy(), p.scales.copy()
+    nb = K // 32
+    for n, E in enumerate((0, 1, 2, 253, 254) * 3):           # rows 0..14: one special block
+        blk = n % nb
+        e[n, blk] = E
+        if E >= 253:
+            ks = [k for k in range(32 * blk, 32 * blk + 32) if np.all(np.abs(xf[:, k]) < 1.0)]
+            q[n, 32 * blk:32 * blk + 32] = 0
+            q[n, ks[n % len(ks)]] = 1                            # E2M1 code 1 = 0.5
+    e[15:24] = rng.integers(0, 3, size=(9, nb))                  # rows 15..23: every block tiny
+    for n in range(15, 20):                                      # rows 15..19: subnormal results
+        q[n] = 0
+        for blk in (n % nb, (n + 3) % nb):
+            e[n, blk] = 0
+            ks = [k for k in range(32 * blk, 32 * blk + 32) if np.all(np.abs(xf[:, k]) < 1.0)]
+            q[n, ks[n % len(ks)]] = 1
+    nan_rows = [24, 31, 47]
+    for n in nan_rows:
+        e[n, n % nb] = 255
+    p.w_packed = gen.pack(q, 4)
+    p.scales = e
+    w, s = _dev(p)
+    U.say("mxfp4 special scale exponents")
+    y = U.q.mxfp4(w, s, xd[:M], out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    g = y.cpu().numpy().astype(np.float64)
+    is_nan = np.isnan(g)
+    assert np.array_equal(is_nan.any(axis=0), np.isin(np.arange(N), nan_rows)), np.nonzero(is_nan.any(axis=0))
+    assert is_nan[:, nan_rows].all()
+    ok = np.setdiff1d(np.arange(N), nan_rows)
+    assert np.isfinite(g[:, ok]).all()
+    want = _ref(p, xs[:M])
+    mag = oracle.default().qmv_mxfp4_mag(p.scales, xs[:M], x_dtype=oracle.DT["bf16"])
+    d = U.mx_depth(K, "bf16")
+    bound = U.gamma(d) * mag[:, ok] + d * 2.0 ** -149
+    over = np.abs(g[:, ok] - want[:, ok]) > bound
+    assert not over.any(), [(int(m), int(ok[n])) for m, n in zip(*np.nonzero(over))][:8]
+    # rows 15..19 are subnormal results (two terms below 2^-127 each), not flushed to zero
+    tiny = g[:, 15:20]
+    assert np.all(np.abs(tiny) < 2.0 ** -126) and np.all(tiny != 0.0)
+    for m in range(M):
+        one = U.q.mxfp4(w, s, xd[m:m + 1], out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(y[m]), _bits(one[0])), f"vector {m}"
