@@ -110,12 +110,20 @@ int make_plan(int M, int N, int K, int bits, int gs, bool xf32, bool sbf, int R,
     const bool copies_fit = per * m_slot <= qmv::kMetaBytes && sb_bytes <= (1LL << 31) - 16;
     const long long static_lds = (long long)qmv::kMaxWaves * 2 * qmv::kMetaBytes;
     // per vector and window: padded activations and a float2 per chunk
-    // (dot-chain start, group sum)
+    // (dot-chain start, group sum).  Padding: 16 bytes after every 256.  With
+    // one window a vector's slot holds the row's chunks and one zero chunk
+    // after them (which the lanes past the row's end read), not the whole last
+    // wave step; with more, every window's chunks (the last window's zero
+    // chunk lies inside its slot).
+    auto phys = [](long long o) { return o + ((o >> 8) << 4); };
+    auto slot_bytes = [&](int w) -> int {
+        if (w < nsteps) return (int)phys((long long)w * qmv::kWave * xcb);
+        return (int)phys((long long)chunks * xcb) + (chunks < w * qmv::kWave ? xcb : 0);
+    };
     int ws = nsteps, x_m = 0, sc_bytes = 0;
     long long total = 0;
     for (;;) {
-        const int logical = ws * qmv::kWave * xcb;
-        x_m = logical + logical / 16;
+        x_m = slot_bytes(ws);
         sc_bytes = M * ws * qmv::kWave * 8;
         total = (long long)M * x_m + sc_bytes;
         if (total <= qmv::kLdsBytes || ws == 1) break;
@@ -124,11 +132,8 @@ int make_plan(int M, int N, int K, int bits, int gs, bool xf32, bool sbf, int R,
     if (total > qmv::kLdsBytes) return QMV_E_SHAPE;
     const int nwin = (nsteps + ws - 1) / ws;
     ws = (nsteps + nwin - 1) / nwin;  // even windows
-    {
-        const int logical = ws * qmv::kWave * xcb;
-        x_m = logical + logical / 16;
-        sc_bytes = M * ws * qmv::kWave * 8;
-    }
+    x_m = nwin == 1 ? slot_bytes(ws) : (int)phys((long long)ws * qmv::kWave * xcb);
+    sc_bytes = M * ws * qmv::kWave * 8;
     Params& p = pl.p;
     p.N = N;
     p.K = K;

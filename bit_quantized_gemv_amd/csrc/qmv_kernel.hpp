@@ -110,7 +110,8 @@ struct Params {
     int nwin;            // K windows
     int n_rb;            // row blocks of W*R rows
     int y_bf16;          // y: 1 = bf16, 0 = fp32
-    int x_m_bytes;       // LDS bytes of one vector's activation window (padded)
+    int x_m_bytes;       // LDS bytes of one vector's activation window (padded); with one
+                         // window, only the row's chunks and one zero chunk after them
     int s_off;           // LDS offset of SC[M][win_steps * 64]: per chunk a float2 (dot-chain
                          // start -2^bits * chunk sum for bf16 activations, 0 for fp32;
                          // sum of the chunk's group)
@@ -441,12 +442,15 @@ struct Stager {
         if (valid && (l % UPC) == 0) SC[m * p.win_steps * kWave + l / UPC] = make_float2(c0, part);
     }
 
-    // zero the activations, chain starts and group sums of the window's chunks
-    // past the row's end (only the last window of a row has them)
+    // zero the activations past the window's chunks -- with one window only the
+    // chunk after them, which the lanes past the row's end read; with several,
+    // the rest of the last window's slot -- and the chain starts and group
+    // sums of the window's chunks past the row's end (only the last window of
+    // a row has them)
     __device__ void zero_tail(const Params& p, uint8_t* lds) const
     {
-        const int pieces = (p.win_steps * kWave - c_n) * XCB / 16;
         const int cw = p.win_steps * kWave;
+        const int pieces = (p.nwin > 1) ? (cw - c_n) * XCB / 16 : (c_n < cw) ? XCB / 16 : 0;
         float2* SC = reinterpret_cast<float2*>(lds + p.s_off);
 #pragma unroll
         for (int m = 0; m < M; ++m) {
@@ -865,6 +869,18 @@ void qmv_affine_kernel(const Params p, Stamps... stamp_ptr)
     };
     meta_block(0);
     const int xl = lds_phys(lane * XCB);          // LDS offset of the lane's chunk in a window's first step
+    // Lanes past the row's end (the last step of the last window) read the zero
+    // chunk that follows that window's chunks: every valid chunk's offset is
+    // below it, so one minimum does the clamp.  (Computed here from loaded
+    // arguments: a further kernel argument regrouped the argument loads into a
+    // serial pair, +2.5% at one vector.)
+    const int xz = lds_phys((p.chunks - (p.nwin - 1) * cwin) * XCB);
+    // (K-windowed layouts keep every window's slot whole, with its tail zeroed,
+    // so only a one-window layout clamps.)  Held per lane, as the room between
+    // the lane's first-step offset and the limit: a scalar kept across the
+    // unit loop costs the windowed instances two more scalar-register reloads
+    // per unit.
+    const int xroom = ((WIN && p.nwin > 1) ? 0x3fffffff : xz) - xl;
     for (int ub = 0; ub < n_units; ub += NS) {
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
@@ -962,7 +978,8 @@ void qmv_affine_kernel(const Params p, Stamps... stamp_ptr)
                         own_select();
                     }
                 };
-                const int xo0 = xl + c_tw * XSTEP;            // chunk's LDS offset (never straddles padding)
+                // chunk's LDS offset (never straddles padding); past the row's end the zero chunk
+                const int xo0 = xl + min(c_tw * XSTEP, xroom);
                 const int cl = c_tw * kWave + lane;           // chunk within the window
 
                 if constexpr (!XF32) {

@@ -108,16 +108,22 @@ def test_more_than_one_tile_of_vectors(name):
 
 
 def test_long_k_vectors_cut_into_whole_k_tiles():
-    # 13 vectors of K = 5120 do not fit LDS whole; with 17408 rows each
-    # workgroup walks several row blocks, so the call runs as two whole-K
-    # launches (7 + 6 vectors) instead of one K-windowed launch
-    assert U.q.kernel_info(13, 17408, 5120, 4, 64)["k_windows"] == 1
+    # K = 6144 (three full wave steps): 13 vectors' activations do not fit LDS
+    # whole; with 17408 rows each workgroup walks several row blocks, so the
+    # call runs as two whole-K launches (7 + 6 vectors) instead of one
+    # K-windowed launch
+    assert U.q.kernel_info(13, 17408, 6144, 4, 64)["k_windows"] == 1
     # few rows: one row block per workgroup, so windowing is kept
-    assert U.q.kernel_info(13, 256, 5120, 4, 64)["k_windows"] > 1
+    assert U.q.kernel_info(13, 256, 6144, 4, 64)["k_windows"] > 1
+    # K = 5120 ends half-way through its third wave step: a vector's slot holds
+    # the row's 160 chunks and one zero chunk (10,944 bytes, not three padded
+    # steps' 13,056), so 13 vectors fit one whole-K launch
+    info = U.q.kernel_info(13, 17408, 5120, 4, 64)
+    assert info["k_windows"] == 1 and info["lds_bytes"] >= 13 * 10944, info
     # vectors still equal their one-vector calls through the tiled launches
-    p = gen.make_problem("up_4b_17408x5120")
+    p = gen.make_problem(N=17408, K=6144, bits=4, gs=64, sb="bf16", x_dtype="bf16", seed=61)
     dev = U.to_dev(p)
-    U.say("whole-K tiles up_4b_17408x5120 M=13")
+    U.say("whole-K tiles 17408x6144 M=13")
     y = U.gpu(p, dev, 13, torch.float32)
     for m in (0, 6, 7, 12):
         one = U.gpu(p, dev, 1, torch.float32, x=dev[3][m:m + 1])
