@@ -15,7 +15,8 @@
 //   * Chunk c (16 bytes = 32 codes = one block) of a row is read by lane c % 64
 //     in wave step c / 64; a wavefront owns R consecutive rows; a workgroup of
 //     W wavefronts stages x[0..M)[0..K) in LDS (its own dtype, natural order,
-//     zero past the row's last chunk) and walks row blocks of W*R rows.
+//     one zero chunk past the row's last, which the lanes past the row's end
+//     read) and walks row blocks of W*R rows.
 //   * Per row, chunk and vector: the codes of each byte become an exact bf16
 //     pair (v_cvt_scalef32_pk_bf16_fp4 with scale 1: low nibble first); D is
 //     the v_dot2_f32_bf16 chain over the chunk's 16 pairs, in byte order,
@@ -51,8 +52,9 @@ struct MxParams {
     int y_bf16;
     int win_steps;   // wave steps per K window (even unless one window covers K)
     int nwin;        // K windows
-    int xm_bytes;    // LDS bytes of one vector's window (win_steps*64 chunks of 64 B, padded)
-    uint32_t ipm_magic;  // i / (16-byte pieces per vector and window) is
+    int xm_bytes;    // LDS bytes of one vector's slot, padded: a window's chunks (win_steps*64),
+                     // or with the whole K the row's chunks and one zero chunk (at most nsteps*64)
+    uint32_t ipm_magic;  // i / (16-byte pieces per vector slot) is
     int ipm_shift;       // umulhi(i, ipm_magic) >> ipm_shift for every staging index i
 };
 
@@ -130,6 +132,9 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void qmv_mx_kernel(MxParams p)
     // are issued before any store; the first batch of the first window carries
     // the first weight step behind it.
     const int cwin = p.win_steps * kWave;                 // chunks per window
+    // Chunks in a vector's LDS slot: a window's, or with the whole K the row's
+    // and one zero chunk after them (which the lanes past the row's end read)
+    const int cslot = WIN ? cwin : min(p.chunks + 1, cwin);
     constexpr int XB = XF32 ? 4 : 2;                      // activation bytes
     constexpr int PSH = XF32 ? 3 : 2;                     // log2 of 16-byte pieces per chunk
     constexpr int PPC = 1 << PSH;
@@ -140,14 +145,14 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void qmv_mx_kernel(MxParams p)
     // more than the second batch a long window then needs
     constexpr int SB = (M == 1) ? 2 : (M == 2 ? 4 : 8);
     auto stage = [&](int win, auto first_tag) {
-        const int items = M * cwin * PPC;
+        const int items = M * cslot * PPC;
         const int c0 = win * cwin;
         auto batch = [&](int i0, auto with_issue) {
             uint4 v[SB];
 #pragma unroll
             for (int j = 0; j < SB; ++j) {
                 const int i = min(i0 + j * (int)blockDim.x + (int)threadIdx.x, items - 1);
-                const int m = (int)(__umulhi((uint32_t)i, p.ipm_magic) >> p.ipm_shift), rem = i - m * (cwin * PPC);
+                const int m = (int)(__umulhi((uint32_t)i, p.ipm_magic) >> p.ipm_shift), rem = i - m * (cslot * PPC);
                 const int c = min(c0 + (rem >> PSH), p.chunks - 1), piece = rem & (PPC - 1);
                 v[j] = buf_load(xr, (m * p.K + c * 32) * XB + piece * 16);
             }
@@ -156,7 +161,7 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void qmv_mx_kernel(MxParams p)
             for (int j = 0; j < SB; ++j) {
                 const int i = i0 + j * (int)blockDim.x + (int)threadIdx.x;
                 if (i < items) {
-                    const int m = (int)(__umulhi((uint32_t)i, p.ipm_magic) >> p.ipm_shift), rem = i - m * (cwin * PPC);
+                    const int m = (int)(__umulhi((uint32_t)i, p.ipm_magic) >> p.ipm_shift), rem = i - m * (cslot * PPC);
                     const int cl = rem >> PSH, piece = rem & (PPC - 1);
                     const uint4 d = (c0 + cl < p.chunks) ? v[j] : make_uint4(0, 0, 0, 0);
                     *reinterpret_cast<uint4*>(lds + m * p.xm_bytes + lds_phys(cl * CB + piece * 16)) = d;
@@ -195,7 +200,8 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void qmv_mx_kernel(MxParams p)
             float sc[R];
 #pragma unroll
             for (int r = 0; r < R; ++r) sc[r] = e8m0_to_f32(eb[slot][r] & 0xffu);
-            const uint8_t* xs = lds + lds_phys(cl * CB);
+            // (whole K: lanes past the row's end read the zero chunk)
+            const uint8_t* xs = lds + lds_phys((WIN ? cl : min(cl, p.chunks)) * CB);
             if constexpr (!XF32) {
                 uint32_t pr[R][16];
 #pragma unroll
@@ -351,6 +357,17 @@ int mx_step_bytes(bool xf32) { return qmv::kWave * 32 * (xf32 ? 4 : 2) * 17 / 16
 
 int mx_steps(int K) { return (K / 32 + qmv::kWave - 1) / qmv::kWave; }
 
+// LDS bytes of one vector's activations with the whole K: the row's chunks and
+// one zero chunk after them (16 bytes of padding after every 256), at most the
+// whole wave steps
+int mx_whole_bytes(int K, bool xf32)
+{
+    const long long cb = 32LL * (xf32 ? 4 : 2);
+    const long long cs = std::min<long long>(K / 32 + 1, (long long)mx_steps(K) * qmv::kWave);
+    const long long o = cs * cb;
+    return (int)(o + ((o >> 8) << 4));
+}
+
 // Rows per wavefront: four (activations read once per four rows) when M >= 3
 // and the row blocks still cover every compute unit, else two.  A K-windowed
 // launch also takes four when two would give workgroups more than one row
@@ -377,8 +394,7 @@ struct MxShape {
 MxShape mx_shape(int M, int N, int K, int cus, bool xf32)
 {
     const int tile = xf32 ? kMxF32Tile : QMV_TILE_M;
-    const int nsteps = mx_steps(K);
-    const int whole = kMxLds / (nsteps * mx_step_bytes(xf32));
+    const int whole = kMxLds / mx_whole_bytes(K, xf32);
     const int Mt = std::min(M, tile);
     if (whole >= Mt) return {tile, 0};
     const int n_rb4 = (N + kMxW * 4 - 1) / (kMxW * 4);
@@ -461,7 +477,7 @@ extern "C" int qmv_mxfp4(const uint32_t* w_packed, const uint8_t* scales, const 
     for (int i = 0; i < 2; ++i) {
         const int Mt = sizes[i];
         if (Mt < 1) continue;
-        const bool win = shape.win_steps > 0 && Mt * mx_steps(K) * step_bytes > kMxLds;
+        const bool win = shape.win_steps > 0 && Mt * mx_whole_bytes(K, xf32) > kMxLds;
         const int R = xf32 ? 2 : mx_rows(Mt, N, cus, win);
         qmv::MxParams& p = plans[i].p;
         p.w = w_packed;
@@ -475,14 +491,16 @@ extern "C" int qmv_mxfp4(const uint32_t* w_packed, const uint8_t* scales, const 
         p.y_bf16 = (y_dt == QMV_DT_BF16) ? 1 : 0;
         p.win_steps = win ? shape.win_steps : p.nsteps;
         p.nwin = (p.nsteps + p.win_steps - 1) / p.win_steps;
-        p.xm_bytes = p.win_steps * step_bytes;
+        p.xm_bytes = win ? p.win_steps * step_bytes : mx_whole_bytes(K, xf32);
         {
             // exact division by d = pieces per vector and window for every
             // index below 2^21 (at most 13 * 2^14 here): with k >= 21 +
             // ceil(log2 d) and magic = ceil(2^k / d), i * d < 2^k makes
             // floor(i * magic / 2^k) = floor(i / d); k >= 32 keeps it one
             // high-half multiply, and magic < 2^32
-            const uint32_t d = (uint32_t)p.win_steps * qmv::kWave * (xf32 ? 8u : 4u);
+            const uint32_t cslot = win ? (uint32_t)p.win_steps * qmv::kWave
+                                       : (uint32_t)std::min(p.chunks + 1, p.nsteps * qmv::kWave);
+            const uint32_t d = cslot * (xf32 ? 8u : 4u);
             int lg = 0;
             while ((1u << lg) < d) ++lg;
             const int k = std::max(32, 21 + lg);
