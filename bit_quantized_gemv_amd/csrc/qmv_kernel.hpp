@@ -340,12 +340,13 @@ struct Stager {
     static constexpr int UPC = VPC / UV;                      // units per chunk
     static constexpr int NLD = (XF32 || BITS == 2) ? 2 : 1;   // 16-byte loads per unit
     // Rounds in flight per batch: 4 at one or two vectors, 8 to six, 16 beyond
-    // (halved where a unit is two loads); from ten vectors with bf16
+    // (halved where a unit is two loads); from nine vectors with bf16
     // activations exactly M, so a window whose vectors take one round each is
-    // one batch with no clamped re-reads (measured 0.3-6% faster at M = 10-13
-    // on the four 4-bit projection shapes and 2-3.5% on the 2-bit one; batches
-    // of M rounds at M = 3-8 were slower).
-    static constexpr int XB = (M >= 10 && (NLD == 1 || (!XF32 && BITS == 2))) ? M : ((M <= 2) ? 4 : (M <= 6 ? 8 : 16)) / NLD;
+    // one batch with no clamped re-reads, and one whose vectors take two is two
+    // equal batches (measured 0.3-7% faster at M = 9-13 on the four 4-bit
+    // projection shapes and 2-4% on the 2-bit one; at M = 7 and 8 mixed, -2%
+    // to +2%, and at M = 3 slower).
+    static constexpr int XB = (M >= 9 && (NLD == 1 || (!XF32 && BITS == 2))) ? M : ((M <= 2) ? 4 : (M <= 6 ? 8 : 16)) / NLD;
 
     int nthr;     // threads in the workgroup
     int upm;      // units per vector in this window
