@@ -40,11 +40,14 @@ Other modes (one JSON line per point instead of the bench line):
                      mxfp4 mode on the four projection shapes
     --sweep-rows     rows per wavefront 1-4 at M = 1, 4, 8, 13 on the 27B-class
                      shapes, with VGPRs, LDS, grid and wavefronts per SIMD
+    --sweep-launch   the launch shape (rows per wavefront, wavefronts and row
+                     blocks per workgroup) of the five workloads at M = 1 and 2
+                     (--sweep-launch-m to choose), beside the library's launch
     --sweep-ceiling  the streaming-read ceiling over the launch shape, at the
                      4-bit and the 2-bit one-vector byte counts
-    --timeline       per-wavefront timelines of the 4-bit projection shapes at
-                     M = 1 and 13 (stamped instance of the same kernel), with
-                     cold and cache-hot activations
+    --timeline       per-wavefront timelines of the 4-bit projection shapes and
+                     the 2-bit up-projection at M = 1 and 13 (stamped instance of
+                     the same kernel), with cold and cache-hot activations
 """
 from __future__ import annotations
 
@@ -355,6 +358,68 @@ def sweep_rows(args, q, gen, torch, np, dev):
         torch.cuda.empty_cache()
 
 
+def sweep_launch(args, q, gen, torch, np, dev):
+    """The launch shape at few vectors (--sweep-launch-m, default 1 and 2) on
+    the five projection workloads: rows per wavefront R, wavefronts per
+    workgroup W in {4, 6, 8} and row blocks per workgroup in {1, 2, 3, 4}, each
+    run through qmv_affine_shape (the library's kernels with that launch; the
+    outputs equal the library's launch bit for bit, checked per point) and
+    timed as the bench line, beside the library's own launch.  One JSON line
+    per point; `default` marks the library's launch."""
+    settled = False
+    for name in ("up_4b_15360x3840", "down_4b_3840x15360", "up_2b_15360x3840",
+                 "up_4b_17408x5120", "down_4b_5120x17408"):
+        p = gen.make_problem(name)
+        N, K, bits, gs = p.N, p.K, p.bits, p.gs
+        nc = max(2, -(-ROTATE_BYTES // alg_bytes(N, K, bits, gs, 13)))
+        copies, ptrs = device_problem(p, torch, np, dev, nc)
+        lib_launch = affine_launcher(q, p, ptrs)
+        if not settled:
+            settle_clocks(lib_launch, nc, torch)
+            settled = True
+        for M in args.sweep_launch_m:
+            nb = alg_bytes(N, K, bits, gs, M)
+            lib_launch(0, M, torch.cuda.current_stream())
+            torch.cuda.synchronize()
+            ref = copies[0][4][:M].clone()
+            us, _ = time_calls(lib_launch, nc, M, args.steps, args.warmup, torch)
+            kinf = q.kernel_info(M, N, K, bits, gs)
+            print(json.dumps({"sweep": "launch_shape", "workload": name, "M": M, "default": True,
+                              "R": kinf["rows_per_wave"], "W": kinf["wg_size"] // 64, "grid": kinf["grid"],
+                              "us_per_call": round(us, 3), "GB/s": round(nb / (us * 1e-6) / 1e9, 1)}),
+                  flush=True)
+            for R in ((1, 2, 3, 4) if bits == 4 else (1, 2)):
+                for W in (4, 6, 8):
+                    for per in (1, 2, 3, 4):
+                        info = q.KernelInfo()
+
+                        def launch(i, MM, stream, R=R, W=W, per=per, info=info):
+                            w, s_, b, x, y = ptrs[i]
+                            st = q.shape_ptr(w, s_, b, x, y, MM, N, K, bits, gs, q.DT_BF16, q.DT_BF16,
+                                             q.DT_BF16, R, W, per, info, stream.cuda_stream)
+                            if st != 0:
+                                raise q.QmvError(st, "qmv_affine_shape")
+                        copies[0][4].zero_()
+                        try:
+                            launch(0, M, torch.cuda.current_stream())
+                        except q.QmvError as e:
+                            print(json.dumps({"sweep": "launch_shape", "workload": name, "M": M, "R": R,
+                                              "W": W, "row_blocks_per_wg": per, "error": str(e)}), flush=True)
+                            continue
+                        torch.cuda.synchronize()
+                        if not torch.equal(copies[0][4][:M], ref):
+                            raise RuntimeError(f"{name} M={M} R={R} W={W} per={per}: output differs")
+                        us, _ = time_calls(launch, nc, M, args.steps, args.warmup, torch)
+                        print(json.dumps({"sweep": "launch_shape", "workload": name, "M": M, "R": R, "W": W,
+                                          "row_blocks_per_wg": per, "grid": info.grid,
+                                          "vgprs": info.vgprs, "waves_per_simd": info.waves_per_simd,
+                                          "lds_bytes": info.lds_bytes, "k_windows": info.k_windows,
+                                          "us_per_call": round(us, 3),
+                                          "GB/s": round(nb / (us * 1e-6) / 1e9, 1)}), flush=True)
+        del copies
+        torch.cuda.empty_cache()
+
+
 def sweep_ceiling(args, q, gen, torch, np, dev):
     """The streaming-read ceiling over the one-vector byte counts of the bench
     line's workload (33,216,000 B) and of the 2-bit 15360 x 3840 workload
@@ -539,6 +604,10 @@ def main():
     ap.add_argument("--sweep-rows", action="store_true",
                     help="instead of the bench line, time rows per wavefront 1-4 at M = 1, 4, 8, 13 on "
                          "the 27B-class shapes, with resources and occupancy per point")
+    ap.add_argument("--sweep-launch", action="store_true",
+                    help="time the launch shape (rows, wavefronts and row blocks per workgroup) at few vectors")
+    ap.add_argument("--sweep-launch-m", type=lambda v: tuple(int(t) for t in v.split(",")), default=(1, 2),
+                    help="vector counts of --sweep-launch (comma-separated)")
     ap.add_argument("--sweep-ceiling", action="store_true",
                     help="instead of the bench line, sweep the streaming-read ceiling's launch shape "
                          "over the 4-bit and 2-bit one-vector byte counts")
@@ -566,6 +635,9 @@ def main():
         return
     if args.sweep_rows:
         sweep_rows(args, q, gen, torch, np, dev)
+        return
+    if args.sweep_launch:
+        sweep_launch(args, q, gen, torch, np, dev)
         return
     if args.sweep_ceiling:
         sweep_ceiling(args, q, gen, torch, np, dev)

@@ -6,8 +6,8 @@ The compute path is the HIP library ``lib/libqmv.so`` (C ABI in
 """
 from .qmv import (QmvError, affine, affine_ptr, kernel_info, status_string, library_path, lib,
                   stream_read_ptr, stream_read_ex_ptr, mxfp4, mxfp4_ptr, timeline, timeline_ptr,
-                  TimelineInfo, STAMPS, DT_F32, DT_F16, DT_BF16, MAX_M)
+                  shape_ptr, KernelInfo, TimelineInfo, STAMPS, DT_F32, DT_F16, DT_BF16, MAX_M)
 
 __all__ = ["QmvError", "affine", "affine_ptr", "kernel_info", "status_string", "library_path", "lib",
            "stream_read_ptr", "stream_read_ex_ptr", "mxfp4", "mxfp4_ptr", "timeline", "timeline_ptr",
-           "TimelineInfo", "STAMPS", "DT_F32", "DT_F16", "DT_BF16", "MAX_M"]
+           "shape_ptr", "KernelInfo", "TimelineInfo", "STAMPS", "DT_F32", "DT_F16", "DT_BF16", "MAX_M"]

@@ -288,12 +288,15 @@ int busiest_cu_rows(const Plan& pl, int cus)
 //   * M <= 2, bound by memory: 8 wavefronts, one unit in flight, and the rows
 //     per wavefront that put the fewest rows on the busiest compute unit
 //     (ties: 2, 3, 1, 4 rows; one row's many small workgroups measure slower
-//     than three rows at equal rows per CU).  Two rows on most shapes; three
-//     on 5120 rows (214 workgroups of 24 rows instead of 320 of 16, 16%
-//     faster); one on 17408 rows (726 workgroups of three 8-row blocks, at
-//     most 72 rows per CU, instead of 363 workgroups of two 24-row blocks,
-//     which leave 107 CUs with two workgroups and 96 rows: 14% faster at one
-//     vector); fewer wavefronts when 8 do not fit.
+//     than three rows at equal rows per CU; fewer wavefronts when 8 do not
+//     fit) -- then, for 4-bit codes, one workgroup per compute unit at four or
+//     three rows where that keeps the busiest unit's rows (below).  Four rows
+//     on 15360 rows (240 workgroups of two 32-row blocks, 64 rows per CU, as
+//     two-row workgroups have); two on 3840 (240 workgroups of 16 rows); three
+//     on 5120 (214 workgroups of 24 rows instead of 320 of 16, 16% faster) and
+//     on 17408 (242 workgroups of three 24-row blocks, 72 rows per CU; by row
+//     count alone one row per wavefront in 726 workgroups, which beat 363
+//     workgroups of two 24-row blocks by 14%); two on the 2-bit shapes.
 //   * M >= 3, bound by the vector ALUs: 8 wavefronts, one unit in flight, and
 //     the R that minimises the rows the busiest compute unit processes,
 //     weighted by the per-row cost of fewer rows per wavefront (the
@@ -330,6 +333,39 @@ int choose_plan(int M, int N, int K, int bits, int gs, bool xf32, bool sbf, int 
                     best = pl;
                 }
                 break;
+            }
+        }
+        // One workgroup of eight wavefronts per compute unit, with four (else
+        // three) rows per wavefront, where that puts no more rows on the
+        // busiest compute unit: no second workgroup stages its activations
+        // behind the first one's weight requests, and 8 x R KiB of weights
+        // stay in flight per compute unit, 24-32 KiB at R = 3-4.  Measured
+        // (bench.py --sweep-launch, two boxes): 15360 x 3840, R = 4, 240
+        // workgroups of two row blocks: 3-4% faster at M = 1 and 5.5% at M = 2
+        // than 480 two-row workgroups; 17408 x 5120, R = 3, 242 workgroups of
+        // three blocks: 2-3% and 5.5-8.6% faster than 726 one-row workgroups.
+        // (At two rows, 16 KiB in flight, one workgroup per compute unit is
+        // slower: 2-bit 15360 x 3840, 5-7%.)
+        if (found && bits == 4) {
+            for (int R : {4, 3}) {
+                if (R_req != 0 && R != R_req) continue;
+                constexpr int W = qmv::kMaxWaves;
+                const int n_rb = (N + W * R - 1) / (W * R);
+                const int per = (n_rb + cus - 1) / cus;
+                Plan pl;
+                if (make_plan(M, N, K, bits, gs, xf32, sbf, R, W, 1, per, pl) != QMV_OK || pl.fn == nullptr)
+                    continue;
+                int nb = 0, scratch = 0;
+                if (!occupancy(reinterpret_cast<const void*>(pl.fn), W, pl.lds, dev, nb, scratch)) return QMV_E_LAUNCH;
+                if (nb == 0) continue;
+                pl.grid = (n_rb + per - 1) / per;
+                pl.blocks_per_cu = nb;
+                pl.p.rb_per = (n_rb + pl.grid - 1) / pl.grid;
+                pl.p.rb_full = n_rb - (pl.p.rb_per - 1) * pl.grid;
+                if (busiest_cu_rows(pl, cus) <= best_rows) {
+                    best = pl;
+                    break;
+                }
             }
         }
         if (found) return QMV_OK;
@@ -490,6 +526,67 @@ int qmv_kernel_info(int M, int N, int K, int bits, int group_size, qmv_dtype x_d
     out->k_windows = pl.p.nwin;
     out->prefetch_units = pl.PF;
     out->meta_lds = pl.p.m_slot > 0 ? 1 : 0;
+    return QMV_OK;
+}
+
+int qmv_affine_shape(const uint32_t* w_packed, const void* scales, const void* biases,
+                     const void* x, void* y, int M, int N, int K, int bits, int group_size,
+                     qmv_dtype x_dt, qmv_dtype sb_dt, qmv_dtype y_dt, int rows_per_wave,
+                     int waves_per_wg, int row_blocks_per_wg, qmv_kernel_info_t* info, void* stream)
+{
+    if (rows_per_wave < 1) return QMV_E_ROWS;
+    int st = check_args(w_packed, scales, biases, x, y, M, N, K, bits, group_size, x_dt, sb_dt,
+                        y_dt, rows_per_wave);
+    if (st != QMV_OK) return st;
+    if (bits == 2 && rows_per_wave >= 3) return QMV_E_ROWS;    // no three- or four-row 2-bit instances
+    if (waves_per_wg < 1 || waves_per_wg > qmv::kMaxWaves || row_blocks_per_wg < 1) return QMV_E_SHAPE;
+    const bool xf32 = (x_dt == QMV_DT_F32);
+    const bool sbf = (sb_dt == QMV_DT_BF16);
+    // one launch: at most the vectors qmv_affine_ex launches together
+    const int mc = tile_vectors(M, N, K, bits, group_size, xf32, sbf, rows_per_wave);
+    if (mc < 1) return QMV_E_SHAPE;
+    if (mc < M) return QMV_E_M_RANGE;
+    Plan pl;
+    st = make_plan(M, N, K, bits, group_size, xf32, sbf, rows_per_wave, waves_per_wg, 1, row_blocks_per_wg, pl);
+    if (st != QMV_OK) return st;
+    if (pl.fn == nullptr) return QMV_E_ROWS;
+    int dev = 0, nb = 0, scratch = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return QMV_E_LAUNCH;
+    if (!occupancy(reinterpret_cast<const void*>(pl.fn), waves_per_wg, pl.lds, dev, nb, scratch)) return QMV_E_LAUNCH;
+    if (nb == 0) return QMV_E_LAUNCH;
+    // workgroups of row_blocks_per_wg row blocks each (the last ones one fewer
+    // where the count does not divide)
+    const int n_rb = pl.p.n_rb;
+    pl.grid = (n_rb + row_blocks_per_wg - 1) / row_blocks_per_wg;
+    pl.blocks_per_cu = nb;
+    pl.p.rb_per = (n_rb + pl.grid - 1) / pl.grid;
+    pl.p.rb_full = n_rb - (pl.p.rb_per - 1) * pl.grid;
+    if (info) {
+        hipFuncAttributes attr;
+        if (hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(pl.fn)) != hipSuccess) return QMV_E_LAUNCH;
+        const int cus = cu_count(dev);
+        info->vgprs = attr.numRegs;
+        info->scratch_bytes = (int)attr.localSizeBytes;
+        info->lds_bytes = pl.lds + (int)attr.sharedSizeBytes;
+        info->wg_size = waves_per_wg * qmv::kWave;
+        info->grid = pl.grid;
+        info->waves_per_simd = (std::min(nb, (pl.grid + cus - 1) / cus) * waves_per_wg + 3) / 4;
+        info->rows_per_wave = rows_per_wave;
+        info->k_windows = pl.p.nwin;
+        info->prefetch_units = pl.PF;
+        info->meta_lds = pl.p.m_slot > 0 ? 1 : 0;
+    }
+    Params& p = pl.p;
+    p.w = w_packed;
+    p.s = static_cast<const uint16_t*>(scales);
+    p.b = static_cast<const uint16_t*>(biases);
+    p.x = x;
+    p.y = y;
+    p.y_bf16 = (y_dt == QMV_DT_BF16);
+    void* args[] = {&p};
+    if (hipLaunchKernel(reinterpret_cast<const void*>(pl.fn), dim3(pl.grid), dim3(waves_per_wg * qmv::kWave), args,
+                        (size_t)pl.lds, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return QMV_E_LAUNCH;
     return QMV_OK;
 }
 

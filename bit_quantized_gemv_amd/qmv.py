@@ -69,6 +69,9 @@ def lib():
         L.qmv_affine_timeline.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, P, ctypes.c_longlong,
                                           ctypes.POINTER(TimelineInfo), P]
         L.qmv_affine_timeline.restype = I
+        L.qmv_affine_shape.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, I, I, I, I,
+                                       ctypes.POINTER(KernelInfo), P]
+        L.qmv_affine_shape.restype = I
         _lib = L
     return _lib
 
@@ -193,6 +196,15 @@ def affine(w, scales, biases, x, *, bits: int, group_size: int, out=None, out_dt
     if status != 0:
         raise QmvError(status, "qmv_affine_ex")
     return out[0] if squeeze else out
+
+
+def shape_ptr(w, s, b, x, y, M, N, K, bits, group_size, x_dt, sb_dt, y_dt, rows_per_wave,
+              waves_per_wg, row_blocks_per_wg, info=None, stream=0) -> int:
+    """Raw C-ABI call of one launch with its launch shape given (a measurement
+    aid for sweeping it); info, if given, is a KernelInfo filled by the call."""
+    return lib().qmv_affine_shape(w, s, b, x, y, M, N, K, bits, group_size, x_dt, sb_dt, y_dt,
+                                  rows_per_wave, waves_per_wg, row_blocks_per_wg,
+                                  None if info is None else ctypes.byref(info), stream)
 
 
 def timeline_ptr(w, s, b, x, y, M, N, K, bits, group_size, y_dt, rows_per_wave, stamps,

@@ -225,6 +225,24 @@ int qmv_affine_timeline(const uint32_t* w_packed, const void* scales, const void
                         qmv_dtype y_dt, int rows_per_wave, uint64_t* stamps, long long stamps_len,
                         qmv_timeline_info_t* info, void* stream);
 
+/* Measurement aid, not part of the product: one launch of the qmv_affine_ex
+ * kernels with its launch shape given instead of chosen -- rows_per_wave R in
+ * 1..4 (1..2 for 2-bit codes), waves_per_wg W in 1..8 wavefronts per
+ * workgroup, and row_blocks_per_wg: each workgroup walks that many row blocks
+ * of W*R rows (the last workgroups one fewer where it does not divide), so the
+ * grid is ceil(ceil(N / (W*R)) / row_blocks_per_wg) workgroups.  For sweeping
+ * the launch shape; the per-row arithmetic does not depend on R, W or the
+ * grid, so y is bit-identical to qmv_affine_ex's.  Arguments, ownership and
+ * numerics as for qmv_affine_ex; M must fit one launch (else QMV_E_M_RANGE);
+ * QMV_E_ROWS for an R with no instance, QMV_E_SHAPE for W or row_blocks_per_wg
+ * out of range or activations that do not fit LDS, QMV_E_LAUNCH if no
+ * workgroup of that shape is resident.  info (host memory, optional) receives
+ * the launch as qmv_kernel_info describes one.  Asynchronous on `stream`. */
+int qmv_affine_shape(const uint32_t* w_packed, const void* scales, const void* biases,
+                     const void* x, void* y, int M, int N, int K, int bits, int group_size,
+                     qmv_dtype x_dt, qmv_dtype sb_dt, qmv_dtype y_dt, int rows_per_wave,
+                     int waves_per_wg, int row_blocks_per_wg, qmv_kernel_info_t* info, void* stream);
+
 /*
  * mxfp4 mode: y = qmv(x) with FP4 (E2M1) codes and one E8M0 scale per block of
  * 32 values along K, no bias:

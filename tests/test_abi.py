@@ -26,7 +26,7 @@ def L():
 
 
 def test_header_declares_the_boundary():
-    assert declared_functions() == ["qmv_affine", "qmv_affine_ex", "qmv_affine_timeline",
+    assert declared_functions() == ["qmv_affine", "qmv_affine_ex", "qmv_affine_shape", "qmv_affine_timeline",
                                     "qmv_kernel_info", "qmv_mxfp4", "qmv_status_string",
                                     "qmv_stream_read", "qmv_stream_read_ex"]
 
@@ -116,6 +116,21 @@ def test_timeline_validates(L):
     assert tl(st=Y) == 9 and tl(st=W + 8) == 9     # stamps overlap y / the weights
     # the checks end here: the next step asks the runtime for the device
     # (QMV_E_LAUNCH without a GPU)
+
+
+def test_shape_launch_validates(L):
+    # the launch with a given shape: host checks before any HIP call
+    def sh(w=W, s=SC, b=BI, x=X, y=Y, M=1, N=256, K=512, bits=4, gs=64, R=2, Wv=8, per=1):
+        return L.qmv_affine_shape(w, s, b, x, y, M, N, K, bits, gs, 2, 2, 2, R, Wv, per, None, None)
+    assert sh(R=0) == 8                            # QMV_E_ROWS: the rows per wavefront are given
+    assert sh(R=5) == 8
+    assert sh(bits=2, gs=128, R=3) == 8            # no three-row 2-bit instances
+    assert sh(w=0) == 1
+    assert sh(K=96) == 4
+    assert sh(Wv=0) == 4 and sh(Wv=9) == 4         # at most eight wavefronts per workgroup
+    assert sh(per=0) == 4
+    assert sh(y=X) == 9
+    # the checks end here: the next step asks the runtime for the device
 
 
 def _tensors(N=4, K=512, bits=4, gs=64, M=1):

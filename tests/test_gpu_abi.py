@@ -1,7 +1,9 @@
 """The C ABI on the GPU: qmv_affine (the bf16 entry point) called directly
 through ctypes, against qmv_affine_ex and the oracle; the binding's argument
-checks raising before anything is launched; and the mxfp4 mode's special
-E8M0 scale bytes (0, 1, 2, 253, 254 and NaN) against the oracle."""
+checks raising before anything is launched; the mxfp4 mode's special
+E8M0 scale bytes (0, 1, 2, 253, 254 and NaN) against the oracle; and the
+launch with a given shape (qmv_affine_shape) bit for bit against the
+library's own launch."""
 import ctypes
 
 import numpy as np
@@ -127,3 +129,37 @@ def test_mxfp4_special_scale_bytes():
             err = np.abs(sub[m] - ref[m])
             assert np.max(err) <= 2e-5 * np.max(np.abs(ref[m])), (scale, m)
             assert np.all(err <= U.gamma(U.mx_depth(K, "bf16")) * mag[m, rows] + 64 * 2.0 ** -150), (scale, m)
+
+
+@pytest.mark.parametrize("spec,M", [((1000, 1984, 4), 1), ((1000, 1984, 4), 5), ((777, 2176, 2), 3),
+                                    ("up_4b_15360x3840", 1), ("down_4b_3840x15360", 13)])
+def test_shape_launch_matches_the_library(spec, M):
+    """qmv_affine_shape with a given rows per wavefront, workgroup size and row
+    blocks per workgroup writes the bits qmv_affine_ex writes: the per-row
+    arithmetic does not depend on the launch shape."""
+    if isinstance(spec, str):
+        p = gen.make_problem(spec)
+    else:
+        N, K, bits = spec
+        p = gen.make_problem(N=N, K=K, bits=bits, gs=64 if bits == 4 else 128, sb="bf16", x_dtype="bf16",
+                             seed=N + K)
+    w, s, b, x = U.to_dev(p)
+    xm = x[:M].contiguous()
+    y = U.q.affine(w, s, b, xm, bits=p.bits, group_size=p.gs, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    Rs = (1, 2, 3, 4) if p.bits == 4 else (1, 2)
+    for R in Rs:
+        for Wv in (3, 8):
+            for per in (1, 3):
+                U.say(f"shape launch {spec} M={M} R={R} W={Wv} per={per}")
+                out = torch.full((M, p.N), float("nan"), dtype=torch.float32, device=U.DEV)
+                info = U.q.KernelInfo()
+                st = U.q.shape_ptr(w.data_ptr(), s.data_ptr(), b.data_ptr(), xm.data_ptr(), out.data_ptr(),
+                                   M, p.N, p.K, p.bits, p.gs, U.q.DT_BF16, U.q.DT_BF16, U.q.DT_F32,
+                                   R, Wv, per, info, torch.cuda.current_stream().cuda_stream)
+                torch.cuda.synchronize()
+                assert st == 0, (R, Wv, per, st)
+                assert info.wg_size == 64 * Wv and info.rows_per_wave == R
+                n_rb = -(-p.N // (Wv * R))
+                assert info.grid == -(-n_rb // per)
+                assert torch.equal(out.view(torch.int32), y.view(torch.int32)), (R, Wv, per)

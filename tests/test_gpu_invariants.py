@@ -131,11 +131,11 @@ def test_long_k_vectors_cut_into_whole_k_tiles():
 
 
 @pytest.mark.parametrize("M,N,K,bits,gs,R,grid", [
-    (1, 15360, 3840, 4, 64, 2, 480),     # bench shape: two rows, two row blocks per workgroup
+    (1, 15360, 3840, 4, 64, 4, 240),     # bench shape: four rows, one workgroup of two row blocks per CU
     (13, 15360, 3840, 4, 64, 4, 240),    # bench shape at 13 vectors: four rows
     (1, 5120, 17408, 4, 64, 3, 214),     # 5120 rows: three rows spread over 214 CUs
     (13, 5120, 17408, 4, 64, 3, 214),
-    (1, 17408, 5120, 4, 64, 1, 726),     # 17408 rows: one row, three 8-row blocks per workgroup
+    (1, 17408, 5120, 4, 64, 3, 242),     # 17408 rows: three rows, one workgroup of three blocks per CU
     (1, 15360, 3840, 2, 128, 2, 480),    # 2 bits: two rows
 ])
 def test_launch_shape_choices(M, N, K, bits, gs, R, grid):
